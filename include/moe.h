@@ -1,0 +1,204 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts FFN forward pass.
+ *
+ * The layer (Kimi K3 pages):
+ *  - "Kimi K3: The Open Model That Just Cornered the AI Frontier", section
+ *    "Mixture-of-Experts with Dynamic Load Balancing": each token's hidden
+ *    vector goes through a linear gate to one logit per expert, a softmax over
+ *    the experts, and a top-k that returns the selected values and indices.
+ *  - "Kimi K3: Open Frontier Intelligence", section "Operational Execution
+ *    Flow": a token's routed output is the sum over its selected experts of the
+ *    gate probability times that expert's output; the expert FFNs have SwiGLU's
+ *    form (the SiTU-GLU sentence names the SwiGLU regime it keeps).
+ *  - same page, section "Systems Optimization, Load Balancing, and
+ *    Post-Training Alignment": per-expert token counts vary from step to step,
+ *    and waiting on them on the host stalls the device; nothing here reads
+ *    counts back to the host.
+ *
+ * Conventions shared by every call
+ *  - All tensors are dense, row-major (C order), on the device, 16-byte
+ *    aligned. bfloat16 values are passed as uint16_t bit patterns.
+ *  - Weights are stored output-major, input-contiguous (the layout of a linear
+ *    layer's weight): w_router [E, d] float32; w_gate, w_up [E, h, d] bf16;
+ *    w_down [E, d, h] bf16. So logits = x w_router^T, gate = x w_gate[e]^T.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues kernels on it and returns; nothing is synchronised, nothing is
+ *    copied to the host, nothing is allocated or freed by the library. The
+ *    caller owns every buffer, including the workspace.
+ *  - Arguments are checked on the host before any launch. On error nothing is
+ *    launched and a status other than MOE_OK is returned; moe_last_error()
+ *    gives a message (thread-local). T == 0 is a successful no-op.
+ *  - Calls on different streams may overlap when their buffers are disjoint.
+ *  - Shapes: T >= 0 tokens; hidden width d and expert width h are multiples
+ *    of 128; 1 <= E <= 1024 experts; 1 <= k <= min(E, 64); T * k < 2^31.
+ *  - Results are deterministic: the same inputs give bitwise the same outputs
+ *    (no floating-point atomics anywhere).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef struct moe_shape {
+    int64_t T; /* tokens in the batch */
+    int32_t d; /* hidden width */
+    int32_t E; /* routed experts */
+    int32_t k; /* experts selected per token */
+    int32_t h; /* hidden width of one SwiGLU expert */
+} moe_shape_t;
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad shape */
+    MOE_ERR_UNSUPPORTED = 2, /* valid but outside the sizes this build handles */
+    MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = 4          /* a HIP launch failed (message from the runtime) */
+} moe_status_t;
+
+/* Which call a workspace size is asked for. */
+typedef enum moe_call {
+    MOE_CALL_PERMUTE = 0,
+    MOE_CALL_EXPERT_FFN = 1,
+    MOE_CALL_FORWARD = 2
+} moe_call_t;
+
+/* Intermediates that moe_forward keeps in its workspace (see moe_forward_ws_offset). */
+typedef enum moe_fwd_slot {
+    MOE_FWD_LOGITS = 0,         /* float   [T, E]   */
+    MOE_FWD_TOPK_IDX = 1,       /* int32   [T, k]   */
+    MOE_FWD_TOPK_W = 2,         /* float   [T, k]   */
+    MOE_FWD_EXPERT_OFFSETS = 3, /* int32   [E + 1]  */
+    MOE_FWD_ROW_OF = 4,         /* int32   [T, k]   */
+    MOE_FWD_ROW_SRC = 5,        /* int32   [T * k]  */
+    MOE_FWD_X_PERM = 6,         /* bf16    [T * k, d] */
+    MOE_FWD_H = 7,              /* bf16    [T * k, h] */
+    MOE_FWD_Y = 8,              /* float   [T * k, d] */
+    MOE_FWD_NUM_SLOTS = 9
+} moe_fwd_slot_t;
+
+/* Version of this ABI (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* moe_status_str(int status);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Bytes of workspace that `call` (a moe_call_t) needs for this shape; 0 when the
+ * shape is invalid (moe_last_error() then says why). Workspace must be 256-byte aligned. */
+size_t moe_workspace_bytes(const moe_shape_t* shape, int call);
+
+/* Byte offset inside moe_forward's workspace of one intermediate (slot is a
+ * moe_fwd_slot_t), so a caller can read what the forward pass computed.
+ * Returns MOE_OK or MOE_ERR_INVALID_ARG. */
+int moe_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset);
+
+/*
+ * moe_route -- gate logits, softmax over experts, top-k, renormalised weights.
+ * Gate: "Kimi K3: The Open Model That Just Cornered the AI Frontier", section
+ * "Mixture-of-Experts with Dynamic Load Balancing" (linear gate, softmax, top-k).
+ *
+ *  x           [T, d]  bf16    token hidden vectors (read)
+ *  w_router    [E, d]  float32 gate weight (read)
+ *  router_bias [E]     float32 added to every token's logits, or NULL (read)
+ *  logits      [T, E]  float32 out: x w_router^T + bias, float32 accumulation of
+ *                      exact bf16 x float32 products
+ *  topk_idx    [T, k]  int32   out: slot j = expert with the j-th largest logit;
+ *                      equal logits (and -0.0 vs +0.0) go to the lower expert id
+ *  topk_w      [T, k]  float32 out: softmax probabilities of the selected experts,
+ *                      renormalised to sum to 1 (exp(l_j - l_0) / sum_i exp(l_i - l_0))
+ * NaN logits are outside the contract; the ids written are still k distinct
+ * experts in [0, E).
+ */
+int moe_route(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
+              const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
+              void* stream);
+
+/*
+ * moe_topk_softmax -- the second half of moe_route on caller-supplied float32
+ * logits: softmax over experts, top-k, renormalised weights, with the same
+ * selection and tie rules as moe_route (same section of the same page).
+ *
+ *  logits   [T, E] float32 (read)
+ *  topk_idx [T, k] int32   (written)
+ *  topk_w   [T, k] float32 (written)
+ */
+int moe_topk_softmax(const moe_shape_t* shape, const float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream);
+
+/*
+ * moe_permute -- group the T*k (token, slot) assignments by expert, stably, and
+ * gather the token rows into expert order (the "grouped by expert" dispatch).
+ *
+ *  x              [T, d]   bf16  (read)
+ *  topk_idx       [T, k]   int32 expert of each assignment, in [0, E) (read);
+ *                          an id outside [0, E) is skipped: its row_of entry is -1
+ *  expert_offsets [E + 1]  int32 out: rows of expert e are expert_offsets[e] ..
+ *                          expert_offsets[e+1]-1; expert_offsets[0] = 0
+ *  row_of         [T, k]   int32 out: row that holds assignment (t, j)
+ *  row_src        [T * k]  int32 out: token of each row
+ *  x_perm         [T * k, d] bf16 out: x_perm[r] = x[row_src[r]]
+ *  ws, ws_bytes   workspace of at least moe_workspace_bytes(shape, MOE_CALL_PERMUTE)
+ * Within an expert, rows follow the flattened assignment index t*k + j.
+ */
+int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_idx,
+                int32_t* expert_offsets, int32_t* row_of, int32_t* row_src, uint16_t* x_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn -- every expert's SwiGLU FFN on its rows (grouped GEMM on bf16
+ * MFMA with float32 accumulation). "Kimi K3: Open Frontier Intelligence",
+ * section "Operational Execution Flow" (SwiGLU-form experts).
+ *
+ *  x_perm         [T * k, d] bf16 rows grouped by expert (read)
+ *  expert_offsets [E + 1]    int32 as written by moe_permute (read; only the
+ *                            device copy is used, the host never sees it)
+ *  w_gate, w_up   [E, h, d]  bf16 (read)
+ *  w_down         [E, d, h]  bf16 (read)
+ *  h_act          [T * k, h] bf16 out: silu(x w_gate[e]^T) * (x w_up[e]^T), rounded once
+ *  y_rows         [T * k, d] float32 out: h_act w_down[e]^T (float32 accumulation)
+ *  ws, ws_bytes   workspace of at least moe_workspace_bytes(shape, MOE_CALL_EXPERT_FFN)
+ */
+int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm,
+                   const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                   const uint16_t* w_down, uint16_t* h_act, float* y_rows, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- out[t] = sum_{j=0}^{k-1} topk_w[t, j] * y_rows[row_of[t, j]],
+ * float32 accumulation in slot order, no atomics. "Kimi K3: Open Frontier
+ * Intelligence", section "Operational Execution Flow" (weighted sum of experts).
+ *
+ *  y_rows [T * k, d] float32 (read); row_of [T, k] int32 (read; -1 entries are
+ *  skipped); topk_w [T, k] float32 (read); out [T, d] float32 (written).
+ */
+int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of,
+                const float* topk_w, float* out, void* stream);
+
+/*
+ * moe_forward -- the whole layer: moe_route, moe_permute, moe_expert_ffn and
+ * moe_combine in sequence on one stream, intermediates in the workspace at the
+ * offsets moe_forward_ws_offset() gives.
+ *
+ *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL;
+ *  w_gate, w_up [E, h, d] bf16; w_down [E, d, h] bf16 (all read)
+ *  out [T, d] float32 (written)
+ *  ws, ws_bytes  workspace of at least moe_workspace_bytes(shape, MOE_CALL_FORWARD)
+ */
+int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
+                const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                const uint16_t* w_down, float* out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,89 @@
+"""ctypes binding of libmoe.so: the C ABI declared in include/moe.h, same names.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. If libmoe.so is missing or does not load, importing this module
+raises; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+MOE_CALL_PERMUTE = 0
+MOE_CALL_EXPERT_FFN = 1
+MOE_CALL_FORWARD = 2
+
+FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "x_perm", "h_act", "y_rows"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("h", ctypes.c_int32)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_mixture_experts_fp32_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    S = ctypes.POINTER(MoeShape)
+    sig = {
+        "moe_abi_version": (ctypes.c_int, []),
+        "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_last_error": (ctypes.c_char_p, []),
+        "moe_workspace_bytes": (ctypes.c_size_t, [S, ctypes.c_int]),
+        "moe_forward_ws_offset": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_route": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
+        "moe_topk_softmax": (ctypes.c_int, [S, P, P, P, P]),
+        "moe_permute": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_combine": (ctypes.c_int, [S, P, P, P, P, P]),
+        "moe_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def check(status: int) -> None:
+    if status != MOE_OK:
+        msg = lib.moe_last_error().decode() or lib.moe_status_str(status).decode()
+        raise MoEError(status, msg)
+
+
+def shape(T: int, d: int, E: int, k: int, h: int) -> MoeShape:
+    return MoeShape(T, d, E, k, h)
+
+
+def workspace_bytes(s: MoeShape, call: int) -> int:
+    n = lib.moe_workspace_bytes(ctypes.byref(s), call)
+    err = lib.moe_last_error().decode()
+    if n == 0 and err:
+        raise MoEError(MOE_ERR_INVALID_ARG, err)
+    return n
+
+
+def forward_ws_offset(s: MoeShape, slot: int) -> int:
+    off = ctypes.c_size_t(0)
+    check(lib.moe_forward_ws_offset(ctypes.byref(s), slot, ctypes.byref(off)))
+    return off.value

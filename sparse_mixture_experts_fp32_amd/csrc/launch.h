@@ -1,0 +1,31 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
+                              int64_t T, int d, int E, hipStream_t stream);
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
+                               float* topk_w, hipStream_t stream);
+
+hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream);  // fill kernel, safe under graph capture
+int permute_chunk(int64_t n_assign);
+int permute_nchunks(int64_t n_assign);
+hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T, int d, int E, int k,
+                          int32_t* expert_offsets, int32_t* row_of, int32_t* row_src, uint16_t* x_perm,
+                          int32_t* count_ws, hipStream_t stream);
+
+int ffn_tile_rows();
+int ffn_max_tiles(int64_t n_rows, int E);
+hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* expert_offsets, int64_t n_rows, int d,
+                             int E, int h, const uint16_t* w_gate, const uint16_t* w_up,
+                             const uint16_t* w_down, uint16_t* h_act, float* y_rows, int4* tiles,
+                             hipStream_t stream);
+
+hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T,
+                          int d, int k, int64_t n_rows, float* out, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,283 @@
+// C ABI of the routed MoE FFN forward pass: argument checks, workspace layout
+// and kernel launches on the caller's stream. No allocation, no host sync.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+int hip_status(hipError_t err, const char* where) {
+    if (err == hipSuccess) return ok();
+    return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(err));
+}
+
+constexpr size_t kWsAlign = 256;
+
+size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const moe_shape_t* s) {
+    if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %lld < 0", static_cast<long long>(s->T));
+    if (s->E < 1 || s->E > 1024) return fail(MOE_ERR_INVALID_ARG, "E = %d outside [1, 1024]", s->E);
+    if (s->k < 1 || s->k > s->E || s->k > 64)
+        return fail(MOE_ERR_INVALID_ARG, "k = %d outside [1, min(E, 64)] (E = %d)", s->k, s->E);
+    if (s->d < 128 || s->d % 128 != 0 || s->d > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "d = %d is not a positive multiple of 128 (<= 2^20)", s->d);
+    if (s->h < 128 || s->h % 128 != 0 || s->h > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "h = %d is not a positive multiple of 128 (<= 2^20)", s->h);
+    if (s->T * static_cast<int64_t>(s->k) >= (int64_t(1) << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "T * k = %lld >= 2^31", static_cast<long long>(s->T * s->k));
+    if ((s->T + 3) / 4 >= (int64_t(1) << 31) || (s->T + 63) / 64 > 65535)
+        return fail(MOE_ERR_UNSUPPORTED, "T = %lld too large for one launch", static_cast<long long>(s->T));
+    return MOE_OK;
+}
+
+#define MOE_CHECK_PTR(p)                                                               \
+    do {                                                                               \
+        if ((p) == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", #p);        \
+        if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+    if (need == 0) return MOE_OK;
+    if (ws == nullptr) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if ((reinterpret_cast<uintptr_t>(ws) & (kWsAlign - 1)) != 0)
+        return fail(MOE_ERR_WORKSPACE, "workspace is not %zu-byte aligned", kWsAlign);
+    if (ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return MOE_OK;
+}
+
+size_t permute_ws(const moe_shape_t* s) {
+    const int64_t n = s->T * s->k;
+    if (n == 0) return 0;
+    return align_up(sizeof(int32_t) * static_cast<size_t>(s->E) * moe::permute_nchunks(n));
+}
+
+size_t ffn_ws(const moe_shape_t* s) {
+    const int64_t n = s->T * s->k;
+    if (n == 0) return 0;
+    return align_up(sizeof(int4) * static_cast<size_t>(moe::ffn_max_tiles(n, s->E)));
+}
+
+// Byte offsets of every slot of moe_forward's workspace; slot MOE_FWD_NUM_SLOTS
+// holds the permute scratch, the one after it the tile list, then the total.
+void forward_layout(const moe_shape_t* s, size_t off[MOE_FWD_NUM_SLOTS + 3]) {
+    const size_t T = static_cast<size_t>(s->T), E = s->E, k = s->k, d = s->d, h = s->h;
+    const size_t sizes[MOE_FWD_NUM_SLOTS + 2] = {
+        4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k,
+        2 * T * k * d, 2 * T * k * h, 4 * T * k * d, permute_ws(s), ffn_ws(s)};
+    size_t at = 0;
+    for (int i = 0; i < MOE_FWD_NUM_SLOTS + 2; ++i) {
+        off[i] = at;
+        at += align_up(sizes[i]);
+    }
+    off[MOE_FWD_NUM_SLOTS + 2] = at;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_str(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported size";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_workspace_bytes(const moe_shape_t* shape, int call) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    switch (call) {
+        case MOE_CALL_PERMUTE: ok(); return permute_ws(shape);
+        case MOE_CALL_EXPERT_FFN: ok(); return ffn_ws(shape);
+        case MOE_CALL_FORWARD: {
+            size_t off[MOE_FWD_NUM_SLOTS + 3];
+            forward_layout(shape, off);
+            ok();
+            return off[MOE_FWD_NUM_SLOTS + 2];
+        }
+        default: fail(MOE_ERR_INVALID_ARG, "unknown call %d", call); return 0;
+    }
+}
+
+int moe_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (slot < 0 || slot >= MOE_FWD_NUM_SLOTS) return fail(MOE_ERR_INVALID_ARG, "unknown slot %d", slot);
+    if (offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "offset is NULL");
+    size_t off[MOE_FWD_NUM_SLOTS + 3];
+    forward_layout(shape, off);
+    *offset = off[slot];
+    return ok();
+}
+
+int moe_route(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+              float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(x);
+    MOE_CHECK_PTR(w_router);
+    if (router_bias != nullptr && !aligned16(router_bias))
+        return fail(MOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+    MOE_CHECK_PTR(logits);
+    MOE_CHECK_PTR(topk_idx);
+    MOE_CHECK_PTR(topk_w);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, shape->T, shape->d, shape->E, s);
+    if (err != hipSuccess) return hip_status(err, "router_gemm launch");
+    err = moe::launch_topk_softmax(logits, shape->T, shape->E, shape->k, topk_idx, topk_w, s);
+    return hip_status(err, "topk_softmax launch");
+}
+
+int moe_topk_softmax(const moe_shape_t* shape, const float* logits, int32_t* topk_idx, float* topk_w,
+                     void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(logits);
+    MOE_CHECK_PTR(topk_idx);
+    MOE_CHECK_PTR(topk_w);
+    hipError_t err = moe::launch_topk_softmax(logits, shape->T, shape->E, shape->k, topk_idx, topk_w,
+                                              static_cast<hipStream_t>(stream));
+    return hip_status(err, "topk_softmax launch");
+}
+
+int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_idx, int32_t* expert_offsets,
+                int32_t* row_of, int32_t* row_src, uint16_t* x_perm, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_PTR(expert_offsets);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (shape->T == 0) {  // still a valid empty grouping: all offsets are 0
+        hipError_t err = moe::launch_zero_i32(expert_offsets, shape->E + 1, s);
+        return hip_status(err, "expert_offsets clear");
+    }
+    MOE_CHECK_PTR(x);
+    MOE_CHECK_PTR(topk_idx);
+    MOE_CHECK_PTR(row_of);
+    MOE_CHECK_PTR(row_src);
+    MOE_CHECK_PTR(x_perm);
+    st = check_ws(ws, ws_bytes, permute_ws(shape));
+    if (st != MOE_OK) return st;
+    hipError_t err = moe::launch_permute(x, topk_idx, shape->T, shape->d, shape->E, shape->k, expert_offsets,
+                                         row_of, row_src, x_perm, static_cast<int32_t*>(ws), s);
+    return hip_status(err, "permute launch");
+}
+
+int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm, const int32_t* expert_offsets,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, uint16_t* h_act,
+                   float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(x_perm);
+    MOE_CHECK_PTR(expert_offsets);
+    MOE_CHECK_PTR(w_gate);
+    MOE_CHECK_PTR(w_up);
+    MOE_CHECK_PTR(w_down);
+    MOE_CHECK_PTR(h_act);
+    MOE_CHECK_PTR(y_rows);
+    st = check_ws(ws, ws_bytes, ffn_ws(shape));
+    if (st != MOE_OK) return st;
+    hipError_t err = moe::launch_expert_ffn(x_perm, expert_offsets, shape->T * shape->k, shape->d, shape->E,
+                                            shape->h, w_gate, w_up, w_down, h_act, y_rows,
+                                            static_cast<int4*>(ws), static_cast<hipStream_t>(stream));
+    return hip_status(err, "expert_ffn launch");
+}
+
+int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of, const float* topk_w,
+                float* out, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(y_rows);
+    MOE_CHECK_PTR(row_of);
+    MOE_CHECK_PTR(topk_w);
+    MOE_CHECK_PTR(out);
+    hipError_t err = moe::launch_combine(y_rows, row_of, topk_w, shape->T, shape->d, shape->k,
+                                         shape->T * shape->k, out, static_cast<hipStream_t>(stream));
+    return hip_status(err, "combine launch");
+}
+
+int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
+                size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(x);
+    MOE_CHECK_PTR(w_router);
+    if (router_bias != nullptr && !aligned16(router_bias))
+        return fail(MOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+    MOE_CHECK_PTR(w_gate);
+    MOE_CHECK_PTR(w_up);
+    MOE_CHECK_PTR(w_down);
+    MOE_CHECK_PTR(out);
+    size_t off[MOE_FWD_NUM_SLOTS + 3];
+    forward_layout(shape, off);
+    st = check_ws(ws, ws_bytes, off[MOE_FWD_NUM_SLOTS + 2]);
+    if (st != MOE_OK) return st;
+    char* base = static_cast<char*>(ws);
+    auto at = [&](int slot) { return static_cast<void*>(base + off[slot]); };
+    float* logits = static_cast<float*>(at(MOE_FWD_LOGITS));
+    int32_t* idx = static_cast<int32_t*>(at(MOE_FWD_TOPK_IDX));
+    float* w = static_cast<float*>(at(MOE_FWD_TOPK_W));
+    int32_t* offsets = static_cast<int32_t*>(at(MOE_FWD_EXPERT_OFFSETS));
+    int32_t* row_of = static_cast<int32_t*>(at(MOE_FWD_ROW_OF));
+    int32_t* row_src = static_cast<int32_t*>(at(MOE_FWD_ROW_SRC));
+    uint16_t* x_perm = static_cast<uint16_t*>(at(MOE_FWD_X_PERM));
+    uint16_t* h_act = static_cast<uint16_t*>(at(MOE_FWD_H));
+    float* y_rows = static_cast<float*>(at(MOE_FWD_Y));
+    int32_t* count_ws = static_cast<int32_t*>(at(MOE_FWD_NUM_SLOTS));
+    int4* tiles = static_cast<int4*>(at(MOE_FWD_NUM_SLOTS + 1));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t T = shape->T, n = shape->T * shape->k;
+    const int d = shape->d, E = shape->E, k = shape->k, h = shape->h;
+
+    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, T, d, E, s);
+    if (err != hipSuccess) return hip_status(err, "router_gemm launch");
+    err = moe::launch_topk_softmax(logits, T, E, k, idx, w, s);
+    if (err != hipSuccess) return hip_status(err, "topk_softmax launch");
+    err = moe::launch_permute(x, idx, T, d, E, k, offsets, row_of, row_src, x_perm, count_ws, s);
+    if (err != hipSuccess) return hip_status(err, "permute launch");
+    err = moe::launch_expert_ffn(x_perm, offsets, n, d, E, h, w_gate, w_up, w_down, h_act, y_rows, tiles, s);
+    if (err != hipSuccess) return hip_status(err, "expert_ffn launch");
+    err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
+    return hip_status(err, "combine launch");
+}
+
+}  // extern "C"

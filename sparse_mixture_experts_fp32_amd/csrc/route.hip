@@ -1,0 +1,237 @@
+// Routing: gate logits (a dense contraction on the matrix cores) and the
+// per-token softmax / top-k / renormalisation (one wavefront per token).
+//
+// Gate, softmax and top-k: "Kimi K3: The Open Model That Just Cornered the AI
+// Frontier", section "Mixture-of-Experts with Dynamic Load Balancing".
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- gate GEMM
+//
+// logits[t, e] = sum_i x[t, i] * w[e, i] (+ bias[e]), x bf16, w float32.
+//
+// Every float32 weight is split exactly into three bfloat16 terms,
+// w = hi + mid + lo (8 + 8 + 8 significant bits; the RNE residues are exactly
+// representable), and each product x * part is exact in float32 because both
+// factors carry at most 8 significant bits. The three products accumulate in
+// the MFMA's float32 accumulator, so the result is a float32 accumulation of
+// exact products, on bf16 matrix cores (16x the float32 vector rate).
+//
+// Tile: 64 tokens x 64 experts per 256-thread workgroup, K step 64;
+// wave (wm, wn) owns a 32 x 32 quarter as 2 x 2 blocks of 16 x 16.
+
+constexpr int kRBM = 64, kRBN = 64, kRBK = 64;
+constexpr int kRStride = kRBK + 8;  // bf16 per LDS row: 144 B keeps 16-B reads conflict-free
+
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          const float* __restrict__ bias,
+                                                          float* __restrict__ logits, int64_t T,
+                                                          int d, int E) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kRBM * kRStride];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[3][kRBN * kRStride];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n0 = blockIdx.x * kRBN;
+    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRBM;
+
+    // global -> register staging: thread owns one row and a 16-wide k chunk
+    const int ld_row = tid >> 2, ld_part = tid & 3;
+    const bool a_ok = (m0 + ld_row) < T;
+    const bool b_ok = (n0 + ld_row) < E;
+    const uint16_t* a_src = x + (m0 + ld_row) * static_cast<int64_t>(d) + ld_part * 16;
+    const float* b_src = w + static_cast<int64_t>(n0 + ld_row) * d + ld_part * 16;
+
+    uint4 a_reg[2];
+    float4 b_reg[4];
+    auto load_tile = [&](int k0) {
+        if (a_ok) {
+            a_reg[0] = *reinterpret_cast<const uint4*>(a_src + k0);
+            a_reg[1] = *reinterpret_cast<const uint4*>(a_src + k0 + 8);
+        } else {
+            a_reg[0] = a_reg[1] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            b_reg[q] = b_ok ? *reinterpret_cast<const float4*>(b_src + k0 + 4 * q)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    auto store_tile = [&]() {
+        uint16_t* a_dst = sA + ld_row * kRStride + ld_part * 16;
+        reinterpret_cast<uint4*>(a_dst)[0] = a_reg[0];
+        reinterpret_cast<uint4*>(a_dst)[1] = a_reg[1];
+        uint16_t hi[16], mid[16], lo[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float v[4] = {b_reg[q].x, b_reg[q].y, b_reg[q].z, b_reg[q].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint16_t h = f32_to_bf16_bits(v[c]);
+                const float r1 = v[c] - bf16_bits_to_f32(h);
+                const uint16_t m = f32_to_bf16_bits(r1);
+                const float r2 = r1 - bf16_bits_to_f32(m);
+                hi[4 * q + c] = h;
+                mid[4 * q + c] = m;
+                lo[4 * q + c] = f32_to_bf16_bits(r2);
+            }
+        }
+        const int off = ld_row * kRStride + ld_part * 16;
+        uint16_t* parts[3] = {hi, mid, lo};
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            reinterpret_cast<uint4*>(sB[p] + off)[0] = reinterpret_cast<const uint4*>(parts[p])[0];
+            reinterpret_cast<uint4*>(sB[p] + off)[1] = reinterpret_cast<const uint4*>(parts[p])[1];
+        }
+    };
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
+    load_tile(0);
+    for (int k0 = 0; k0 < d; k0 += kRBK) {
+        store_tile();
+        __syncthreads();
+        if (k0 + kRBK < d) load_tile(k0 + kRBK);
+#pragma unroll
+        for (int s = 0; s < kRBK / 32; ++s) {
+            bf16x8 a[2], b[3][2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 32 + i * 16 + frag_row) * kRStride + s * 32 + frag_k);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    b[p][j] = *reinterpret_cast<const bf16x8*>(sB[p] + (wn * 32 + j * 16 + frag_row) * kRStride + s * 32 + frag_k);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    acc[i][j] = mfma_16x16x32(a[i], b[2][j], acc[i][j]);
+                    acc[i][j] = mfma_16x16x32(a[i], b[1][j], acc[i][j]);
+                    acc[i][j] = mfma_16x16x32(a[i], b[0][j], acc[i][j]);
+                }
+        }
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn * 32 + j * 16 + (lane & 15);
+        if (col >= E) continue;
+        const float bcol = bias ? bias[col] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + q;
+                if (row < T) logits[row * E + col] = acc[i][j][q] + bcol;
+            }
+    }
+}
+
+// ------------------------------------------------------------ softmax + top-k
+//
+// One wavefront per token; lane l holds experts l, l + 64, ... Each logit
+// becomes a 64-bit key whose upper half orders the float value (-0.0 folded
+// onto +0.0, NaN below everything) and whose lower half is ~expert id, so the
+// largest key is the largest logit with ties going to the lower id. k rounds of
+// a wavefront max pick the slots in descending order.
+//
+// Renormalised weights: p_j / sum_{i<k} p_i with p = softmax over all E equals
+// exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0): the softmax denominator cancels,
+// so only the k selected logits are exponentiated.
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v != v) return 0u;     // NaN: below every number
+    if (v == 0.0f) v = 0.0f;   // -0.0 ties +0.0
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+    if (k == 0u) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits,
+                                                           int64_t T, int E, int k,
+                                                           int32_t* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    const float* row = logits + t * E;
+
+    uint64_t key[NPER];
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+        const int e = lane + 64 * i;
+        key[i] = (e < E) ? ((static_cast<uint64_t>(order_key(row[e])) << 32) | (0xffffffffu - static_cast<uint32_t>(e)))
+                         : 0ull;
+    }
+
+    int my_id = 0;
+    float my_val = 0.f;
+    for (int j = 0; j < k; ++j) {
+        uint64_t best = key[0];
+#pragma unroll
+        for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max_u64(best);
+#pragma unroll
+        for (int i = 0; i < NPER; ++i)
+            if (key[i] == best) key[i] = 0ull;  // unique: the low half names one expert
+        if (lane == j) {
+            my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+            my_val = key_value(static_cast<uint32_t>(best >> 32));
+        }
+    }
+    const float top = __shfl(my_val, 0, kWave);
+    const float ex = (lane < k) ? expf(my_val - top) : 0.f;
+    const float sum = wave_sum_f32(ex);
+    if (lane < k) {
+        topk_idx[t * k + lane] = my_id;
+        topk_w[t * k + lane] = ex / sum;
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
+                              int64_t T, int d, int E, hipStream_t stream) {
+    dim3 grid((E + kRBN - 1) / kRBN, static_cast<unsigned>((T + kRBM - 1) / kRBM));
+    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, w, bias, logits, T, d, E);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
+                               float* topk_w, hipStream_t stream) {
+    dim3 grid(static_cast<unsigned>((T + 3) / 4));
+    const int nper = (E + 63) / 64;
+#define MOE_TOPK_CASE(N)                                                                        \
+    case N:                                                                                     \
+        hipLaunchKernelGGL(topk_softmax_kernel<N>, grid, dim3(256), 0, stream, logits, T, E, k, \
+                           topk_idx, topk_w);                                                   \
+        break;
+    switch (nper) {
+        MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
+        MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
+        MOE_TOPK_CASE(9) MOE_TOPK_CASE(10) MOE_TOPK_CASE(11) MOE_TOPK_CASE(12)
+        MOE_TOPK_CASE(13) MOE_TOPK_CASE(14) MOE_TOPK_CASE(15) MOE_TOPK_CASE(16)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef MOE_TOPK_CASE
+    return hipGetLastError();
+}
+
+}  // namespace moe

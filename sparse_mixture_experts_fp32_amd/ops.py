@@ -1,0 +1,201 @@
+"""Torch-tensor front end of libmoe.so.
+
+PyTorch provides device memory and the current stream; every computation
+happens in the library's kernels, reached through the C ABI with the same
+call names (moe_route, moe_permute, moe_expert_ffn, moe_combine, moe_forward).
+Tensors must be contiguous, on one GPU, in the dtypes include/moe.h states.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32, "i32": torch.int32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != _DT[dtype]:
+        raise TypeError(f"{name} must be {_DT[dtype]}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape_of(x, w_router, k, h):
+    T, d = x.shape
+    E = w_router.shape[0]
+    return _lib.shape(T, d, E, k, h)
+
+
+def workspace(s: _lib.MoeShape, call: int, device) -> torch.Tensor:
+    n = _lib.workspace_bytes(s, call)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def moe_route(x, w_router, router_bias, k: int, *, out=None):
+    """Gate logits [T,E] f32, top-k ids [T,k] i32, renormalised weights [T,k] f32."""
+    _need(x, "x", "bf16")
+    dev = x.device
+    T, d = x.shape
+    E = w_router.shape[0]
+    _need(w_router, "w_router", "f32", (E, d), dev)
+    if router_bias is not None:
+        _need(router_bias, "router_bias", "f32", (E,), dev)
+    s = _lib.shape(T, d, E, k, 128)
+    if out is None:
+        out = (torch.empty((T, E), dtype=torch.float32, device=dev),
+               torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty((T, k), dtype=torch.float32, device=dev))
+    logits, idx, w = out
+    _need(logits, "logits", "f32", (T, E), dev)
+    _need(idx, "topk_idx", "i32", (T, k), dev)
+    _need(w, "topk_w", "f32", (T, k), dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                      _ptr(logits), _ptr(idx), _ptr(w), _stream(dev)))
+    return logits, idx, w
+
+
+def moe_topk_softmax(logits, k: int):
+    """Top-k ids [T,k] i32 and renormalised weights [T,k] f32 from given f32 logits [T,E]."""
+    _need(logits, "logits", "f32")
+    dev = logits.device
+    T, E = logits.shape
+    s = _lib.shape(T, 128, E, k, 128)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_topk_softmax(ctypes.byref(s), _ptr(logits), _ptr(idx), _ptr(w), _stream(dev)))
+    return idx, w
+
+
+def moe_permute(x, topk_idx, E: int):
+    """expert_offsets [E+1], row_of [T,k], row_src [T*k] (int32) and x_perm [T*k, d] bf16."""
+    _need(x, "x", "bf16")
+    dev = x.device
+    T, d = x.shape
+    k = topk_idx.shape[1] if topk_idx.dim() == 2 else 1
+    _need(topk_idx, "topk_idx", "i32", (T, k), dev)
+    s = _lib.shape(T, d, E, k, 128)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
+    row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
+    x_perm = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev)
+    ws = workspace(s, _lib.MOE_CALL_PERMUTE, dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_permute(ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(offsets), _ptr(row_of),
+                                        _ptr(row_src), _ptr(x_perm), _ptr(ws), ws.numel(), _stream(dev)))
+    return offsets, row_of, row_src, x_perm
+
+
+def moe_expert_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int):
+    """h_act [T*k, h] bf16 and y_rows [T*k, d] f32 for rows grouped by expert."""
+    _need(x_perm, "x_perm", "bf16")
+    dev = x_perm.device
+    n, d = x_perm.shape
+    if n != T * k:
+        raise ValueError(f"x_perm has {n} rows, expected T*k = {T * k}")
+    E, h, _ = w_gate.shape
+    _need(expert_offsets, "expert_offsets", "i32", (E + 1,), dev)
+    _need(w_gate, "w_gate", "bf16", (E, h, d), dev)
+    _need(w_up, "w_up", "bf16", (E, h, d), dev)
+    _need(w_down, "w_down", "bf16", (E, d, h), dev)
+    s = _lib.shape(T, d, E, k, h)
+    h_act = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+    y_rows = torch.empty((n, d), dtype=torch.float32, device=dev)
+    ws = workspace(s, _lib.MOE_CALL_EXPERT_FFN, dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_expert_ffn(ctypes.byref(s), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate),
+                                           _ptr(w_up), _ptr(w_down), _ptr(h_act), _ptr(y_rows), _ptr(ws),
+                                           ws.numel(), _stream(dev)))
+    return h_act, y_rows
+
+
+def moe_combine(y_rows, row_of, topk_w):
+    """out [T, d] f32 = sum_j topk_w[t, j] * y_rows[row_of[t, j]]."""
+    _need(y_rows, "y_rows", "f32")
+    dev = y_rows.device
+    n, d = y_rows.shape
+    T, k = row_of.shape
+    if n != T * k:
+        raise ValueError(f"y_rows has {n} rows, expected T*k = {T * k}")
+    _need(row_of, "row_of", "i32", (T, k), dev)
+    _need(topk_w, "topk_w", "f32", (T, k), dev)
+    s = _lib.shape(T, d, max(k, 1), k, 128)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_combine(ctypes.byref(s), _ptr(y_rows), _ptr(row_of), _ptr(topk_w), _ptr(out),
+                                        _stream(dev)))
+    return out
+
+
+class MoEForward:
+    """moe_forward with a reusable workspace (allocated once per shape)."""
+
+    def __init__(self, T: int, d: int, E: int, k: int, h: int, device):
+        self.shape = _lib.shape(T, d, E, k, h)
+        self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
+        self.device = torch.device(device)
+        self.ws = workspace(self.shape, _lib.MOE_CALL_FORWARD, self.device)
+
+    def __call__(self, x, w_router, router_bias, w_gate, w_up, w_down, out=None):
+        T, d, E, k, h, dev = self.T, self.d, self.E, self.k, self.h, self.device
+        _need(x, "x", "bf16", (T, d), dev)
+        _need(w_router, "w_router", "f32", (E, d), dev)
+        if router_bias is not None:
+            _need(router_bias, "router_bias", "f32", (E,), dev)
+        _need(w_gate, "w_gate", "bf16", (E, h, d), dev)
+        _need(w_up, "w_up", "bf16", (E, h, d), dev)
+        _need(w_down, "w_down", "bf16", (E, d, h), dev)
+        if out is None:
+            out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        _need(out, "out", "f32", (T, d), dev)
+        with torch.cuda.device(dev):
+            _lib.check(_lib.lib.moe_forward(ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                            _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(self.ws),
+                                            self.ws.numel(), _stream(dev)))
+        return out
+
+    def intermediate(self, name: str) -> torch.Tensor:
+        """A view of one intermediate that the last call left in the workspace."""
+        T, d, E, k, h = self.T, self.d, self.E, self.k, self.h
+        spec = {
+            "logits": (torch.float32, (T, E)), "topk_idx": (torch.int32, (T, k)),
+            "topk_w": (torch.float32, (T, k)), "expert_offsets": (torch.int32, (E + 1,)),
+            "row_of": (torch.int32, (T, k)), "row_src": (torch.int32, (T * k,)),
+            "x_perm": (torch.bfloat16, (T * k, d)), "h_act": (torch.bfloat16, (T * k, h)),
+            "y_rows": (torch.float32, (T * k, d)),
+        }
+        dtype, shp = spec[name]
+        off = _lib.forward_ws_offset(self.shape, _lib.FWD_SLOTS.index(name))
+        n = 1
+        for v in shp:
+            n *= v
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype).view(shp)
+
+
+def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, k: int):
+    """One-shot forward (allocates a workspace per call; use MoEForward to reuse one)."""
+    T, d = x.shape
+    E, h, _ = w_gate.shape
+    return MoEForward(T, d, E, k, h, x.device)(x, w_router, router_bias, w_gate, w_up, w_down)

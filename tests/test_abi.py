@@ -1,0 +1,142 @@
+"""CPU tests of the C ABI: the library loads, exports every declared call, and
+rejects bad arguments on the host before anything is launched (no GPU needed:
+each call here fails validation before its first HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "libmoe.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__._build_module().build()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    from sparse_mixture_experts_fp32_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
+              "moe_workspace_bytes", "moe_status_str", "moe_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIB)
+    missing = [n for n in declared_functions() if not hasattr(raw, n)]
+    assert not missing, missing
+    nm = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (moe_\w+)", nm))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(lib):
+    L = lib.lib
+    assert L.moe_abi_version() == 1
+    assert L.moe_status_str(0) == b"ok"
+    for s in range(1, 5):
+        assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
+    assert L.moe_status_str(99) == b"unknown status"
+
+
+GOOD = dict(T=64, d=128, E=8, k=2, h=256)
+
+
+def _shape(lib, **kw):
+    p = dict(GOOD)
+    p.update(kw)
+    return lib.shape(p["T"], p["d"], p["E"], p["k"], p["h"])
+
+
+@pytest.mark.parametrize("bad,status", [
+    (dict(T=-1), 1), (dict(E=0), 1), (dict(E=1025), 1), (dict(k=0), 1), (dict(k=9), 1),
+    (dict(E=100, k=65), 1), (dict(d=96), 1), (dict(d=0), 1), (dict(h=200), 1), (dict(h=-128), 1),
+    (dict(T=2**28, k=8), 2),
+])
+def test_bad_shapes_rejected(lib, bad, status):
+    s = _shape(lib, **bad)
+    fake = ctypes.c_void_p(4096)
+    st = lib.lib.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, fake, None)
+    assert st == status, lib.lib.moe_last_error()
+    assert lib.lib.moe_last_error()
+    assert lib.lib.moe_workspace_bytes(ctypes.byref(s), 2) == 0
+
+
+def test_null_and_misaligned_pointers_rejected(lib):
+    s = _shape(lib)
+    a = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 2)
+    L = lib.lib
+    assert L.moe_route(ctypes.byref(s), None, a, None, a, a, a, None) == 1
+    assert b"x is NULL" in L.moe_last_error()
+    assert L.moe_route(ctypes.byref(s), mis, a, None, a, a, a, None) == 1
+    assert b"aligned" in L.moe_last_error()
+    assert L.moe_route(ctypes.byref(s), a, a, mis, a, a, a, None) == 1
+    assert L.moe_topk_softmax(ctypes.byref(s), None, a, a, None) == 1
+    assert L.moe_combine(ctypes.byref(s), a, a, None, a, None) == 1
+    assert L.moe_expert_ffn(ctypes.byref(s), a, a, a, a, None, a, a, a, 1 << 20, None) == 1
+    assert L.moe_forward(ctypes.byref(s), a, a, None, a, a, a, None, a, 1 << 30, None) == 1
+    assert L.moe_route(None, a, a, None, a, a, a, None) == 1
+
+
+def test_workspace_checks(lib):
+    s = _shape(lib)
+    L = lib.lib
+    a = ctypes.c_void_p(4096)
+    need_p = lib.workspace_bytes(s, lib.MOE_CALL_PERMUTE)
+    need_f = lib.workspace_bytes(s, lib.MOE_CALL_EXPERT_FFN)
+    need_fw = lib.workspace_bytes(s, lib.MOE_CALL_FORWARD)
+    assert need_p > 0 and need_f > 0 and need_fw > 0
+    assert need_p % 256 == 0 and need_f % 256 == 0 and need_fw % 256 == 0
+    assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, None, need_p, None) == 3
+    assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, a, need_p - 1, None) == 3
+    assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, ctypes.c_void_p(4096 + 16), need_p, None) == 3
+    assert L.moe_expert_ffn(ctypes.byref(s), a, a, a, a, a, a, a, a, need_f - 1, None) == 3
+    assert L.moe_forward(ctypes.byref(s), a, a, None, a, a, a, a, a, need_fw - 256, None) == 3
+    assert L.moe_workspace_bytes(ctypes.byref(s), 7) == 0
+
+
+def test_forward_workspace_layout(lib):
+    """Every intermediate fits inside the forward workspace, aligned, without overlap."""
+    for cfg in [GOOD, dict(T=8192, d=7168, E=256, k=4, h=2048), dict(T=16384, d=7168, E=896, k=16, h=1024),
+                dict(T=1, d=128, E=1, k=1, h=128)]:
+        s = lib.shape(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["h"])
+        total = lib.workspace_bytes(s, lib.MOE_CALL_FORWARD)
+        T, d, E, k, h = (cfg[c] for c in "TdEkh")
+        sizes = [4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k, 2 * T * k * d, 2 * T * k * h,
+                 4 * T * k * d]
+        offs = [lib.forward_ws_offset(s, i) for i in range(9)]
+        for i in range(9):
+            assert offs[i] % 256 == 0
+            assert offs[i] + sizes[i] <= total
+            if i + 1 < 9:
+                assert offs[i] + sizes[i] <= offs[i + 1]
+    with pytest.raises(lib.MoEError):
+        lib.forward_ws_offset(lib.shape(64, 128, 8, 2, 256), 9)
+
+
+def test_zero_tokens_is_a_noop(lib):
+    s = _shape(lib, T=0)
+    L = lib.lib
+    assert L.moe_route(ctypes.byref(s), None, None, None, None, None, None, None) == 0
+    assert L.moe_combine(ctypes.byref(s), None, None, None, None, None) == 0
+    assert L.moe_forward(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.moe_expert_ffn(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None) == 0
