@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one pass of the whole layer over one batch: gate logits + top-k
+(moe_route), grouping by expert (moe_permute), the grouped SwiGLU GEMM
+(moe_expert_gate_up, moe_expert_down) and the weighted combine (moe_combine),
+enqueued through the C ABI on one stream with buffers allocated beforehand --
+exactly the kernels moe_forward launches, checked bitwise against it below.
+HIP events on that stream time each GEMM pass inside every timed step.
+
+Prints one JSON line: whole-layer tokens/s, the grouped GEMM's TFLOP/s and
+MFMA fraction, the roofline of the dominant kernel (the gate/up pass) and the
+CPU oracle's rate on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), d=7168 E=256 top-4"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill",
+                    help="named workload (prefill is the headline: T=8192 d=7168 E=256 k=4 h=2048)")
+    ap.add_argument("--cpu-experts", type=int, default=128,
+                    help="experts the CPU oracle runs in its bounded sample (0 = skip the CPU baseline)")
+    return ap.parse_args()
+
+
+class Layer:
+    """Preallocated buffers and C-ABI calls for one workload."""
+
+    def __init__(self, lib, inp, cfg, dev):
+        import torch
+        self.lib, self.inp, self.cfg, self.dev = lib, inp, cfg, dev
+        T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
+        n = T * k
+        e = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        self.logits = e(T, E, dt=torch.float32)
+        self.idx = e(T, k, dt=torch.int32)
+        self.w = e(T, k, dt=torch.float32)
+        self.offsets = e(E + 1, dt=torch.int32)
+        self.row_of = e(T, k, dt=torch.int32)
+        self.row_src = e(n, dt=torch.int32)
+        self.x_perm = e(n, d, dt=torch.bfloat16)
+        self.h_act = e(n, h, dt=torch.bfloat16)
+        self.y_rows = e(n, d, dt=torch.float32)
+        self.out = e(T, d, dt=torch.float32)
+        self.shape = lib.shape(T, d, E, k, h)
+        self.ws_perm = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_PERMUTE)), dt=torch.uint8)
+        self.ws_ffn = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_EXPERT_FFN)), dt=torch.uint8)
+        self.stream = torch.cuda.current_stream(dev)
+        P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.P = P
+        self.sh = ctypes.byref(self.shape)
+        self.sp = ctypes.c_void_p(self.stream.cuda_stream)
+
+    def step(self, ev=None):
+        L, P, sh, sp, i = self.lib.lib, self.P, self.sh, self.sp, self.inp
+        c = self.lib.check
+        c(L.moe_route(sh, P(i.x), P(i.w_router), P(i.router_bias), P(self.logits), P(self.idx), P(self.w), sp))
+        c(L.moe_permute(sh, P(i.x), P(self.idx), P(self.offsets), P(self.row_of), P(self.row_src), P(self.x_perm),
+                        P(self.ws_perm), self.ws_perm.numel(), sp))
+        if ev is not None:
+            ev[0].record(self.stream)
+        c(L.moe_expert_gate_up(sh, P(self.x_perm), P(self.offsets), P(i.w_gate), P(i.w_up), P(self.h_act),
+                               P(self.ws_ffn), self.ws_ffn.numel(), sp))
+        if ev is not None:
+            ev[1].record(self.stream)
+        c(L.moe_expert_down(sh, P(self.h_act), P(self.offsets), P(i.w_down), P(self.y_rows), P(self.ws_ffn),
+                            self.ws_ffn.numel(), sp))
+        if ev is not None:
+            ev[2].record(self.stream)
+        c(L.moe_combine(sh, P(self.y_rows), P(self.row_of), P(self.w), P(self.out), sp))
+
+
+def cpu_baseline(inp, cfg, n_experts):
+    """The oracle, as it is, on the host cores over a bounded sample of the same workload.
+
+    Timed: gate logits, softmax/top-k, permutation, gather and combine over every
+    token, and the SwiGLU FFN of `n_experts` evenly spaced experts with all their
+    rows. The layer time is the measured steps plus the sampled FFN time scaled by
+    (rows of all experts) / (rows of the sampled experts). Copying inputs from the
+    GPU to host memory is input preparation and is not timed.
+    """
+    import numpy as np
+    import torch
+
+    import oracle.moe_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count()
+    E, k = cfg.E, cfg.k
+    x_h = inp.x.cpu()
+    wr_h = inp.w_router.cpu()
+    b_h = None if inp.router_bias is None else inp.router_bias.cpu()
+    sample = sorted({int(round(i * E / n_experts)) % E for i in range(n_experts)})
+    wg = {e: inp.w_gate[e].cpu() for e in sample}
+    wu = {e: inp.w_up[e].cpu() for e in sample}
+    wd = {e: inp.w_down[e].cpu() for e in sample}
+    t = {}
+    t0 = time.perf_counter()
+    L = orc.gate_logits(x_h, wr_h, b_h)
+    t["gate"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    idx, w, _ = orc.route(L, k)
+    t["route"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    off, row_of, row_src = orc.permute(idx, E)
+    t["permute"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    x_perm = orc.gather(x_h, row_src)
+    t["gather"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    H, Y = orc.expert_ffn(x_perm, off, wg, wu, wd, experts=sample)
+    t["ffn_sample"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.combine(np.nan_to_num(Y), row_of, w)
+    t["combine"] = time.perf_counter() - t0
+    rows_all = int(off[-1])
+    rows_sample = int(sum(off[e + 1] - off[e] for e in sample))
+    scale = rows_all / max(rows_sample, 1)
+    layer_s = t["gate"] + t["route"] + t["permute"] + t["gather"] + t["combine"] + t["ffn_sample"] * scale
+    measured = sum(t.values())
+    return {
+        "value": cfg.T / layer_s, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+        "sample": (f"{cfg.name} workload, float64 numpy oracle: gate logits, softmax/top-k, permutation, gather and "
+                   f"combine over all {cfg.T} tokens; SwiGLU experts for {len(sample)} of {E} experts "
+                   f"({rows_sample} of {rows_all} rows), that time scaled by {scale:.2f}; "
+                   f"{measured:.1f} s of CPU work measured, {layer_s:.1f} s estimated per layer"),
+        "torch_threads": torch.get_num_threads(),
+        "seconds": {kk: round(v, 3) for kk, v in t.items()},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): this layer "
+              "build has no multi-GPU path; see the sharding notes in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synthetic import CONFIGS, make_inputs
+    from sparse_mixture_experts_fp32_amd import _lib as lib
+    from sparse_mixture_experts_fp32_amd import MoEForward
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = make_inputs(cfg, device=dev)
+    torch.cuda.synchronize()
+    layer = Layer(lib, inp, cfg, dev)
+
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(layer.stream)
+    for s in range(K):
+        layer.step(evs[s])
+    stop.record(layer.stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / K
+    gpu_ms = start.elapsed_time(stop) / K
+    gate_up_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    down_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+
+    # the step is moe_forward's kernel sequence: same output, bit for bit
+    fwd = MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
+    ref_out = fwd(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_out, layer.out), "bench step and moe_forward disagree"
+    del fwd, ref_out
+
+    T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
+    n = T * k
+    counts = (layer.offsets[1:] - layer.offsets[:-1]).cpu()
+    touched = int((counts > 0).sum())
+    gemm_flops = 6.0 * n * d * h
+    gemm_tflops = gemm_flops / ((gate_up_ms + down_ms) * 1e-3) / 1e12
+    # algorithmic bytes of one gate/up launch: x_perm rows read, touched experts'
+    # gate and up weights read once, H written
+    gu_bytes = 2.0 * n * d + 2.0 * 2 * d * h * touched + 2.0 * n * h
+    gu_gbs = gu_bytes / (gate_up_ms * 1e-3) / 1e9
+    down_bytes = 2.0 * n * h + 2.0 * d * h * touched + 4.0 * n * d
+    down_gbs = down_bytes / (down_ms * 1e-3) / 1e9
+    ms = wall_ms
+    result = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} top-{k} h={h}, SwiGLU experts, fp32 gate",
+                   "T": T, "d": d, "E": E, "k": k, "h": h, "seed": cfg.seed,
+                   "experts_touched": touched, "max_rows_per_expert": int(counts.max())},
+        "gpu_ms_per_step": gpu_ms,
+        "grouped_gemm": {"ms": gate_up_ms + down_ms, "tflops": gemm_tflops,
+                         "mfma_frac": gemm_tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "gate_up_ms": gate_up_ms, "down_ms": down_ms,
+                         "down_gbs": down_gbs, "down_hbm_frac": down_gbs / HBM_PEAK_GBS},
+        "roofline": {"kernel": "grouped_ffn_kernel<gated> (gate/up pass + SwiGLU)", "bound": "hbm",
+                     "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": gu_bytes},
+    }
+    if args.cpu_experts > 0:
+        result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_experts)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -173,6 +173,24 @@ int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm,
                    size_t ws_bytes, void* stream);
 
 /*
+ * moe_expert_gate_up -- the first half of moe_expert_ffn on its own:
+ * h_act[r] = silu(x_perm[r] w_gate[e]^T) * (x_perm[r] w_up[e]^T) for every row r
+ * of expert e, rounded once to bf16. Arguments as in moe_expert_ffn; the
+ * workspace is the same size (MOE_CALL_EXPERT_FFN).
+ */
+int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* x_perm, const int32_t* expert_offsets,
+                       const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_down -- the second half of moe_expert_ffn on its own:
+ * y_rows[r] = h_act[r] w_down[e]^T (float32) for every row r of expert e.
+ * Arguments as in moe_expert_ffn; workspace size MOE_CALL_EXPERT_FFN.
+ */
+int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                    const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_combine -- out[t] = sum_{j=0}^{k-1} topk_w[t, j] * y_rows[row_of[t, j]],
  * float32 accumulation in slot order, no atomics. "Kimi K3: Open Frontier
  * Intelligence", section "Operational Execution Flow" (weighted sum of experts).

@@ -52,6 +52,8 @@ def _load():
         "moe_topk_softmax": (ctypes.c_int, [S, P, P, P, P]),
         "moe_permute": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_gate_up": (ctypes.c_int, [S, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_down": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [S, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     }

@@ -201,23 +201,28 @@ int ffn_max_tiles(int64_t n_rows, int E) {
     return static_cast<int>((t + 7) / 8 * 8);  // multiple of 8 for the XCD map
 }
 
-hipError_t launch_expert_ffn(const uint16_t* x_perm, const int32_t* expert_offsets, int64_t n_rows, int d,
-                             int E, int h, const uint16_t* w_gate, const uint16_t* w_up,
-                             const uint16_t* w_down, uint16_t* h_act, float* y_rows, int4* tiles,
-                             hipStream_t stream) {
-    const int max_tiles = ffn_max_tiles(n_rows, E);
+hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int E, int4* tiles,
+                              hipStream_t stream) {
     hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, stream, expert_offsets, E, n_rows,
-                       ffn_tile_rows(), max_tiles, tiles);
-    {
-        const int n_tiles = (h + 16 * kGemmWaves - 1) / (16 * kGemmWaves);
-        hipLaunchKernelGGL((grouped_ffn_kernel<true, kFfnMSub>), dim3(max_tiles * n_tiles), dim3(kGemmThreads),
-                           0, stream, x_perm, n_rows, tiles, n_tiles, w_gate, w_up, h, d, h_act);
-    }
-    {
-        const int n_tiles = (d + 32 * kGemmWaves - 1) / (32 * kGemmWaves);
-        hipLaunchKernelGGL((grouped_ffn_kernel<false, kFfnMSub>), dim3(max_tiles * n_tiles), dim3(kGemmThreads),
-                           0, stream, h_act, n_rows, tiles, n_tiles, w_down, nullptr, d, h, y_rows);
-    }
+                       ffn_tile_rows(), ffn_max_tiles(n_rows, E), tiles);
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up(const uint16_t* x_perm, const int4* tiles, int64_t n_rows, int d, int E, int h,
+                          const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, hipStream_t stream) {
+    const int max_tiles = ffn_max_tiles(n_rows, E);
+    const int n_tiles = (h + 16 * kGemmWaves - 1) / (16 * kGemmWaves);
+    hipLaunchKernelGGL((grouped_ffn_kernel<true, kFfnMSub>), dim3(max_tiles * n_tiles), dim3(kGemmThreads), 0,
+                       stream, x_perm, n_rows, tiles, n_tiles, w_gate, w_up, h, d, h_act);
+    return hipGetLastError();
+}
+
+hipError_t launch_down(const uint16_t* h_act, const int4* tiles, int64_t n_rows, int d, int E, int h,
+                       const uint16_t* w_down, float* y_rows, hipStream_t stream) {
+    const int max_tiles = ffn_max_tiles(n_rows, E);
+    const int n_tiles = (d + 32 * kGemmWaves - 1) / (32 * kGemmWaves);
+    hipLaunchKernelGGL((grouped_ffn_kernel<false, kFfnMSub>), dim3(max_tiles * n_tiles), dim3(kGemmThreads), 0,
+                       stream, h_act, n_rows, tiles, n_tiles, w_down, nullptr, d, h, y_rows);
     return hipGetLastError();
 }
 

@@ -213,10 +213,57 @@ int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm, const int32
     MOE_CHECK_PTR(y_rows);
     st = check_ws(ws, ws_bytes, ffn_ws(shape));
     if (st != MOE_OK) return st;
-    hipError_t err = moe::launch_expert_ffn(x_perm, expert_offsets, shape->T * shape->k, shape->d, shape->E,
-                                            shape->h, w_gate, w_up, w_down, h_act, y_rows,
-                                            static_cast<int4*>(ws), static_cast<hipStream_t>(stream));
-    return hip_status(err, "expert_ffn launch");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = shape->T * shape->k;
+    int4* tiles = static_cast<int4*>(ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, tiles, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_gate_up(x_perm, tiles, n, shape->d, shape->E, shape->h, w_gate, w_up, h_act, s);
+    if (err != hipSuccess) return hip_status(err, "gate_up launch");
+    err = moe::launch_down(h_act, tiles, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
+    return hip_status(err, "down launch");
+}
+
+int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* x_perm, const int32_t* expert_offsets,
+                       const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, void* ws, size_t ws_bytes,
+                       void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(x_perm);
+    MOE_CHECK_PTR(expert_offsets);
+    MOE_CHECK_PTR(w_gate);
+    MOE_CHECK_PTR(w_up);
+    MOE_CHECK_PTR(h_act);
+    st = check_ws(ws, ws_bytes, ffn_ws(shape));
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = shape->T * shape->k;
+    int4* tiles = static_cast<int4*>(ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, tiles, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_gate_up(x_perm, tiles, n, shape->d, shape->E, shape->h, w_gate, w_up, h_act, s);
+    return hip_status(err, "gate_up launch");
+}
+
+int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                    const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(h_act);
+    MOE_CHECK_PTR(expert_offsets);
+    MOE_CHECK_PTR(w_down);
+    MOE_CHECK_PTR(y_rows);
+    st = check_ws(ws, ws_bytes, ffn_ws(shape));
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = shape->T * shape->k;
+    int4* tiles = static_cast<int4*>(ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, tiles, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_down(h_act, tiles, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
+    return hip_status(err, "down launch");
 }
 
 int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of, const float* topk_w,
@@ -274,8 +321,12 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     if (err != hipSuccess) return hip_status(err, "topk_softmax launch");
     err = moe::launch_permute(x, idx, T, d, E, k, offsets, row_of, row_src, x_perm, count_ws, s);
     if (err != hipSuccess) return hip_status(err, "permute launch");
-    err = moe::launch_expert_ffn(x_perm, offsets, n, d, E, h, w_gate, w_up, w_down, h_act, y_rows, tiles, s);
-    if (err != hipSuccess) return hip_status(err, "expert_ffn launch");
+    err = moe::launch_build_tiles(offsets, n, E, tiles, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_gate_up(x_perm, tiles, n, d, E, h, w_gate, w_up, h_act, s);
+    if (err != hipSuccess) return hip_status(err, "gate_up launch");
+    err = moe::launch_down(h_act, tiles, n, d, E, h, w_down, y_rows, s);
+    if (err != hipSuccess) return hip_status(err, "down launch");
     err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
     return hip_status(err, "combine launch");
 }
