@@ -41,6 +41,9 @@ def parse():
                     help="named workload (prefill is the headline: T=8192 d=7168 E=256 k=4 h=2048)")
     ap.add_argument("--cpu-experts", type=int, default=128,
                     help="experts the CPU oracle runs in its bounded sample (0 = skip the CPU baseline)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="before the steps, run a plain float32 copy kernel (out = -in) over this many MiB three "
+                         "times, so that a counter run can scale FETCH_SIZE / WRITE_SIZE by a known byte count")
     return ap.parse_args()
 
 
@@ -174,6 +177,15 @@ def main():
     inp = make_inputs(cfg, device=dev)
     torch.cuda.synchronize()
     layer = Layer(lib, inp, cfg, dev)
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
 
     for _ in range(args.warmup):
         layer.step()
