@@ -8,6 +8,7 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));  // one MFMA A/B operand
 typedef float f32x4 __attribute__((ext_vector_type(4)));    // one 16x16 MFMA accumulator
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4))); // 16 raw bytes (native vector: stays in registers)
 
 constexpr int kWave = 64;
 

@@ -21,11 +21,12 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
 int ffn_tile_rows();
 int ffn_max_tiles(int64_t n_rows, int E);
 hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int E, int4* tiles,
-                              hipStream_t stream);
-hipError_t launch_gate_up(const uint16_t* x_perm, const int4* tiles, int64_t n_rows, int d, int E, int h,
-                          const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, hipStream_t stream);
-hipError_t launch_down(const uint16_t* h_act, const int4* tiles, int64_t n_rows, int d, int E, int h,
-                       const uint16_t* w_down, float* y_rows, hipStream_t stream);
+                              int32_t* tile_start, hipStream_t stream);
+hipError_t launch_gate_up(const uint16_t* x_perm, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
+                          int d, int E, int h, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
+                          hipStream_t stream);
+hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
+                       int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T,
                           int d, int k, int64_t n_rows, float* out, hipStream_t stream);

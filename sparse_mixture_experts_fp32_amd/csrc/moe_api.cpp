@@ -78,10 +78,25 @@ size_t permute_ws(const moe_shape_t* s) {
     return align_up(sizeof(int32_t) * static_cast<size_t>(s->E) * moe::permute_nchunks(n));
 }
 
+// The grouped GEMM's workspace: the m-tile list, then each expert's first m-tile index.
+size_t ffn_tiles_bytes(const moe_shape_t* s) {
+    return align_up(sizeof(int4) * static_cast<size_t>(moe::ffn_max_tiles(s->T * s->k, s->E)));
+}
+
 size_t ffn_ws(const moe_shape_t* s) {
     const int64_t n = s->T * s->k;
     if (n == 0) return 0;
-    return align_up(sizeof(int4) * static_cast<size_t>(moe::ffn_max_tiles(n, s->E)));
+    return ffn_tiles_bytes(s) + align_up(sizeof(int32_t) * (static_cast<size_t>(s->E) + 1));
+}
+
+struct FfnWs {
+    int4* tiles;
+    int32_t* tile_start;
+};
+
+FfnWs ffn_carve(const moe_shape_t* s, void* ws) {
+    char* b = static_cast<char*>(ws);
+    return FfnWs{reinterpret_cast<int4*>(b), reinterpret_cast<int32_t*>(b + ffn_tiles_bytes(s))};
 }
 
 // Byte offsets of every slot of moe_forward's workspace; slot MOE_FWD_NUM_SLOTS
@@ -215,12 +230,13 @@ int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm, const int32
     if (st != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = shape->T * shape->k;
-    int4* tiles = static_cast<int4*>(ws);
-    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, tiles, s);
+    const FfnWs fw = ffn_carve(shape, ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x_perm, tiles, n, shape->d, shape->E, shape->h, w_gate, w_up, h_act, s);
+    err = moe::launch_gate_up(x_perm, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_gate, w_up,
+                              h_act, s);
     if (err != hipSuccess) return hip_status(err, "gate_up launch");
-    err = moe::launch_down(h_act, tiles, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
     return hip_status(err, "down launch");
 }
 
@@ -239,10 +255,11 @@ int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* x_perm, const i
     if (st != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = shape->T * shape->k;
-    int4* tiles = static_cast<int4*>(ws);
-    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, tiles, s);
+    const FfnWs fw = ffn_carve(shape, ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x_perm, tiles, n, shape->d, shape->E, shape->h, w_gate, w_up, h_act, s);
+    err = moe::launch_gate_up(x_perm, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_gate, w_up,
+                              h_act, s);
     return hip_status(err, "gate_up launch");
 }
 
@@ -259,10 +276,10 @@ int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32
     if (st != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = shape->T * shape->k;
-    int4* tiles = static_cast<int4*>(ws);
-    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, tiles, s);
+    const FfnWs fw = ffn_carve(shape, ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_down(h_act, tiles, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
     return hip_status(err, "down launch");
 }
 
@@ -310,7 +327,7 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     uint16_t* h_act = static_cast<uint16_t*>(at(MOE_FWD_H));
     float* y_rows = static_cast<float*>(at(MOE_FWD_Y));
     int32_t* count_ws = static_cast<int32_t*>(at(MOE_FWD_NUM_SLOTS));
-    int4* tiles = static_cast<int4*>(at(MOE_FWD_NUM_SLOTS + 1));
+    const FfnWs fw = ffn_carve(shape, at(MOE_FWD_NUM_SLOTS + 1));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t T = shape->T, n = shape->T * shape->k;
     const int d = shape->d, E = shape->E, k = shape->k, h = shape->h;
@@ -321,11 +338,11 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     if (err != hipSuccess) return hip_status(err, "topk_softmax launch");
     err = moe::launch_permute(x, idx, T, d, E, k, offsets, row_of, row_src, x_perm, count_ws, s);
     if (err != hipSuccess) return hip_status(err, "permute launch");
-    err = moe::launch_build_tiles(offsets, n, E, tiles, s);
+    err = moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x_perm, tiles, n, d, E, h, w_gate, w_up, h_act, s);
+    err = moe::launch_gate_up(x_perm, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s);
     if (err != hipSuccess) return hip_status(err, "gate_up launch");
-    err = moe::launch_down(h_act, tiles, n, d, E, h, w_down, y_rows, s);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, d, E, h, w_down, y_rows, s);
     if (err != hipSuccess) return hip_status(err, "down launch");
     err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
     return hip_status(err, "combine launch");
