@@ -13,17 +13,19 @@
 // the grid is sized from an upper bound, so no token count ever goes back to
 // the host; surplus workgroups find no work and exit.
 //
-// Inside a workgroup (8 wavefronts): the A rows of the current K step (128
-// deep) are staged in LDS, double-buffered, and shared by all waves; each wave
-// streams its own weight rows straight from HBM into registers, one K step
-// ahead of the matrix cores (each weight byte is used by exactly one wave, so
-// staging it in LDS would buy nothing). Weights are stored [N, K] (K
-// contiguous), so one lane's 8 consecutive k values are a single 16-byte load
-// that is directly an MFMA operand. The K loop is unrolled by two so the two
-// register sets of weights swap roles without copies, and rows past the tile
-// end are clamped to its last row, so every load is unconditional: the wait
-// before each step's MFMAs then covers only that step's weights, never the
-// loads already issued for the next step.
+// Inside a workgroup: the A rows of the current K step are staged in LDS,
+// double-buffered, and shared by all waves; each wave streams its own weight
+// rows straight from HBM into registers, one K step ahead of the matrix cores
+// (each weight byte is used by exactly one wave, so staging it in LDS would buy
+// nothing). Weights are stored [N, K] (K contiguous), so one lane's 8
+// consecutive k values are a single 16-byte load that is directly an MFMA
+// operand. The K loop is unrolled by two so the two register sets of weights
+// swap roles without copies, rows past the tile end are clamped to its last row
+// and the prefetch index is clamped to the last K step, so every load is
+// unconditional and the wait before each step's MFMAs covers only that step's
+// weights, never the loads already issued for the next step. The number of
+// 16-row blocks is a compile-time constant per K loop (one loop per block
+// count, chosen once per tile), so the MFMA sequence is straight-line code.
 //
 // Scheduling for the 8 XCDs (each with its own L2): workgroup ids are dealt to
 // the XCDs round-robin, so XCD x runs ids x, x + 8, x + 16, ... in order. The
@@ -38,12 +40,31 @@
 
 namespace moe {
 
-constexpr int kGemmWaves = 8;
-constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kKStep = 128;
-constexpr int kAStride = kKStep + 8;  // bf16 per LDS row: 272 B keeps 16-B reads conflict-free
 constexpr int kXcds = 8;
-constexpr int kMaxRowBlocks = 8;      // m-tile of up to 128 rows
+constexpr int kFragAhead = 4;  // A fragments read ahead of the MFMAs that consume them
+
+// Tile configuration of one grouped-GEMM kernel. The workgroup's waves form a
+// kWM x kWN grid: wave (wm, wn) owns the 16-row blocks b with b % kWM == wm and
+// kNB blocks of 16 weight rows (gate/up: half gate, half up columns).
+template <int kWM_, int kWN_, int kNB_, int kKS_, int kMaxMB_, bool kDeep_, int kPad_ = 8>
+struct GemmCfg {
+    static constexpr int kWM = kWM_;          // wave rows (split the m-tile's row blocks)
+    static constexpr int kWN = kWN_;          // wave columns (split the n-tile)
+    static constexpr int kNB = kNB_;          // 16-row weight blocks per wave
+    static constexpr int kWaves = kWM * kWN;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kKS = kKS_;          // K step staged per barrier (multiple of 32)
+    static constexpr int kSub = kKS / 32;     // MFMA K sub-steps per K step
+    static constexpr int kAStride = kKS + kPad_;  // bf16 per LDS row (padded against bank conflicts)
+    static constexpr int kMaxMB = kMaxMB_;    // 16-row blocks per m-tile (multiple of kWM)
+    static constexpr int kBM = 16 * kMaxMB;   // rows per m-tile
+    static constexpr int kBufElems = kBM * kAStride;
+    static constexpr int kWRows = 16 * kNB;   // weight rows per wave
+    static constexpr bool kDeep = kDeep_;     // weights 3 K steps ahead, A rows 2 (else 1 and 1)
+    static constexpr int kStepMB = kWM < 2 ? 2 : kWM;  // granularity of the per-tile block count
+    static_assert(kMaxMB % kWM == 0, "row blocks split evenly over wave rows");
+    static_assert(kNB % 2 == 0, "gate/up waves hold matching gate and up blocks");
+};
 
 // One workgroup of 1024 threads; E <= 1024.
 // tiles[i] = {expert, first row, rows, 0} for i < tile_start[E];
@@ -91,118 +112,180 @@ __device__ __forceinline__ void load_rows(u32x4 (&dst)[kP], const uint16_t* src,
     for (int p = 0; p < kP; ++p) dst[p] = *reinterpret_cast<const u32x4*>(src + off[p] + k0);
 }
 
-template <int kP>
+template <int kP, int kStep>
 __device__ __forceinline__ void store_rows(uint16_t* dst, const u32x4 (&src)[kP]) {
 #pragma unroll
-    for (int p = 0; p < kP; ++p) *reinterpret_cast<u32x4*>(dst + p * 32 * kAStride) = src[p];
+    for (int p = 0; p < kP; ++p) *reinterpret_cast<u32x4*>(dst + p * kStep) = src[p];
 }
 
-__device__ __forceinline__ void load_weights(bf16x8 (&dst)[2][4], const uint16_t* w0, const uint16_t* w1, int k0) {
+// dst[b][s]: 16 weight rows of block b, K sub-step s of one K step
+template <int kNB, int kSub>
+__device__ __forceinline__ void load_weights(bf16x8 (&dst)[kNB][kSub], const uint16_t* const (&w)[kNB], int k0) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        dst[0][s] = *reinterpret_cast<const bf16x8*>(w0 + k0 + 32 * s);
-        dst[1][s] = *reinterpret_cast<const bf16x8*>(w1 + k0 + 32 * s);
+    for (int s = 0; s < kSub; ++s)
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) dst[b][s] = *reinterpret_cast<const bf16x8*>(w[b] + k0 + 32 * s);
+}
+
+// acc[b][i] += (A rows of block kWM * i + wm, one K step, from LDS) x (weight block b).
+// The A fragments of the step (kSub x kMBW of them) are read from LDS through a
+// rolling window kFragAhead deep, so each read has that many MFMA groups to land.
+template <int kMBW, int kWM, int kNB, int kSub, int kAStride>
+__device__ __forceinline__ void mfma_step(f32x4 (&acc)[kNB][kMBW], const uint16_t* frag,
+                                          const bf16x8 (&bw)[kNB][kSub]) {
+    constexpr int kF = kSub * kMBW;  // fragments in one K step, f = s * kMBW + i
+    constexpr int kAhead = kF < kFragAhead ? kF : kFragAhead;
+    bf16x8 a[kAhead + 1];
+#pragma unroll
+    for (int f = 0; f < kAhead; ++f)
+        a[f] = *reinterpret_cast<const bf16x8*>(frag + (f % kMBW) * kWM * 16 * kAStride + 32 * (f / kMBW));
+#pragma unroll
+    for (int f = 0; f < kF; ++f) {
+        const int g = f + kAhead;
+        if (g < kF)
+            a[g % (kAhead + 1)] =
+                *reinterpret_cast<const bf16x8*>(frag + (g % kMBW) * kWM * 16 * kAStride + 32 * (g / kMBW));
+        const int i = f % kMBW, s = f / kMBW;
+#pragma unroll
+        for (int b = 0; b < kNB; ++b) acc[b][i] = mfma_16x16x32(a[f % (kAhead + 1)], bw[b][s], acc[b][i]);
     }
-}
-
-// acc[b][m] += (A rows 16m .. 16m+15 of one K step, from LDS) x (weight block b).
-template <int kMB>
-__device__ __forceinline__ void mfma_step(f32x4 (&acc)[2][kMB], const uint16_t* frag, const bf16x8 (&bw)[2][4]) {
+    // Keep that order through instruction scheduling (which would otherwise sink
+    // each read next to its use): kAhead LDS reads, then {kNB MFMAs, 1 LDS read}.
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int m = 0; m < kMB; ++m) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(frag + m * 16 * kAStride + 32 * s);
-            acc[0][m] = mfma_16x16x32(a, bw[0][s], acc[0][m]);
-            acc[1][m] = mfma_16x16x32(a, bw[1][s], acc[1][m]);
-        }
+    for (int f = 0; f < kF; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, kNB, 0);
+        if (f + kAhead < kF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 }
 
 // One (m-tile, n-tile) work item with kMB row blocks of 16 (M <= 16 * kMB rows).
 // Every load and LDS store in the K loop is unconditional: rows past M re-read
-// row M - 1 and the prefetch index is clamped to the last K step (a repeated
-// step is loaded but never used), so the compiler's wait before each MFMA
-// group covers only the weights that group consumes.
-template <bool kGated, int kMB>
+// row M - 1 and prefetch indices are clamped to the last K step (a repeated
+// step is loaded but never used).
+template <class C, bool kGated, int kMB>
 __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restrict__ A, int64_t row0, int M,
-                                         const uint16_t* wb0, const uint16_t* wb1, bool wave_on, int N, int K,
+                                         const uint16_t* const (&wb)[C::kNB], bool wave_on, int N, int K, int wm,
                                          int n_wave, void* __restrict__ Cout) {
-    constexpr int kAPasses = (kMB * 16 + 31) / 32;  // 16 threads x 16 B per row, 32 rows per pass
-    constexpr int kBufElems = 16 * kMaxRowBlocks * kAStride;
+    constexpr int kNB = C::kNB, kSub = C::kSub, kKS = C::kKS;
+    constexpr int kMBW = kMB / C::kWM;   // row blocks of this wave
+    constexpr int kChunks = kKS / 8;     // 16-byte chunks per staged row
+    constexpr int kRowsPerPass = C::kThreads / kChunks;
+    constexpr int kAPasses = (16 * kMB + kRowsPerPass - 1) / kRowsPerPass;
+    static_assert(kMB % C::kWM == 0, "row blocks split evenly over wave rows");
+    static_assert(kAPasses * kRowsPerPass <= C::kBM, "staged rows must fit the LDS tile");
     const int tid = threadIdx.x, lane = tid & 63;
     const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
 
-    const int a_row = tid >> 4, a_col = 8 * (tid & 15);
-    const bool a_on = a_row < 16 * kMB;  // kMB == 1: only the first 16 rows are staged
+    const int a_row = tid / kChunks, a_col = 8 * (tid % kChunks);
     const uint16_t* a_src = A + row0 * K + a_col;
     int64_t a_off[kAPasses];
 #pragma unroll
-    for (int p = 0; p < kAPasses; ++p) a_off[p] = static_cast<int64_t>(min(p * 32 + a_row, M - 1)) * K;
-    uint16_t* a_dst0 = sA + a_row * kAStride + a_col;
-    uint16_t* a_dst1 = a_dst0 + kBufElems;
-    const uint16_t* a_frag0 = sA + frag_row * kAStride + frag_k;
-    const uint16_t* a_frag1 = a_frag0 + kBufElems;
+    for (int p = 0; p < kAPasses; ++p) a_off[p] = static_cast<int64_t>(min(p * kRowsPerPass + a_row, M - 1)) * K;
+    uint16_t* a_dst[2] = {sA + a_row * C::kAStride + a_col, sA + a_row * C::kAStride + a_col + C::kBufElems};
+    const uint16_t* a_frag[2] = {sA + (wm * 16 + frag_row) * C::kAStride + frag_k,
+                                 sA + (wm * 16 + frag_row) * C::kAStride + frag_k + C::kBufElems};
+    constexpr int kPassStride = kRowsPerPass * C::kAStride;
 
-    f32x4 acc[2][kMB];
+    f32x4 acc[kNB][kMBW];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kNB; ++b)
 #pragma unroll
-        for (int m = 0; m < kMB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kMBW; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // K loop over pairs of steps: register sets b0 / b1 and LDS buffers 0 / 1
-    // alternate between "being consumed" and "being filled", without copies.
-    const int nk = K / kKStep;
-    u32x4 a_reg[kAPasses];
-    bf16x8 b0[2][4], b1[2][4];
-    load_rows(a_reg, a_src, a_off, 0);
-    load_weights(b0, wb0, wb1, 0);
-    if (a_on) store_rows(a_dst0, a_reg);
-    __syncthreads();
-    for (int s0 = 0; s0 < nk; s0 += 2) {
-        const int k1 = min(s0 + 1, nk - 1) * kKStep;
-        load_rows(a_reg, a_src, a_off, k1);
-        load_weights(b1, wb0, wb1, k1);
-        if (wave_on) mfma_step(acc, a_frag0, b0);
-        if (a_on) store_rows(a_dst1, a_reg);
+    const int nk = K / kKS;
+    if constexpr (!C::kDeep) {
+        // Weights and A rows one K step ahead: register sets b0 / b1 and LDS
+        // buffers 0 / 1 alternate between "being consumed" and "being filled".
+        u32x4 a_reg[kAPasses];
+        bf16x8 b0[kNB][kSub], b1[kNB][kSub];
+        load_rows(a_reg, a_src, a_off, 0);
+        load_weights(b0, wb, 0);
+        store_rows<kAPasses, kPassStride>(a_dst[0], a_reg);
         __syncthreads();
-        const int k2 = min(s0 + 2, nk - 1) * kKStep;
-        load_rows(a_reg, a_src, a_off, k2);
-        load_weights(b0, wb0, wb1, k2);
-        if (wave_on && s0 + 1 < nk) mfma_step(acc, a_frag1, b1);
-        if (a_on) store_rows(a_dst0, a_reg);
+        for (int s0 = 0; s0 < nk; s0 += 2) {
+            const int k1 = min(s0 + 1, nk - 1) * kKS;
+            load_rows(a_reg, a_src, a_off, k1);
+            load_weights(b1, wb, k1);
+            if (wave_on) mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[0], b0);
+            store_rows<kAPasses, kPassStride>(a_dst[1], a_reg);
+            __syncthreads();
+            const int k2 = min(s0 + 2, nk - 1) * kKS;
+            load_rows(a_reg, a_src, a_off, k2);
+            load_weights(b0, wb, k2);
+            if (wave_on && s0 + 1 < nk) mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[1], b1);
+            store_rows<kAPasses, kPassStride>(a_dst[0], a_reg);
+            __syncthreads();
+        }
+    } else {
+        // Weights three K steps ahead (a ring of four register sets), A rows two
+        // steps ahead (two register sets) and written to LDS one step ahead (two
+        // buffers). Step i: load weights i+3 and A rows i+2, multiply step i,
+        // store A rows i+1, barrier. Four steps per loop trip, so every ring
+        // index is a compile-time constant.
+        u32x4 ar[2][kAPasses];
+        bf16x8 bw[4][kNB][kSub];
+        load_rows(ar[0], a_src, a_off, 0);
+        load_rows(ar[1], a_src, a_off, min(1, nk - 1) * kKS);
+        load_weights(bw[0], wb, 0);
+        load_weights(bw[1], wb, min(1, nk - 1) * kKS);
+        load_weights(bw[2], wb, min(2, nk - 1) * kKS);
+        store_rows<kAPasses, kPassStride>(a_dst[0], ar[0]);
         __syncthreads();
+#define MOE_DEEP_STEP(U)                                                                                  \
+    {                                                                                                     \
+        const int step = s0 + (U);                                                                        \
+        load_weights(bw[((U) + 3) % 4], wb, min(step + 3, nk - 1) * kKS);                                 \
+        load_rows(ar[(U) % 2], a_src, a_off, min(step + 2, nk - 1) * kKS);                                \
+        if (wave_on && step < nk)                                                                         \
+            mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[(U) % 2], bw[(U) % 4]);            \
+        store_rows<kAPasses, kPassStride>(a_dst[((U) + 1) % 2], ar[((U) + 1) % 2]);                       \
+        __syncthreads();                                                                                  \
+    }
+        for (int s0 = 0; s0 < nk; s0 += 4) {
+            MOE_DEEP_STEP(0)
+            MOE_DEEP_STEP(1)
+            MOE_DEEP_STEP(2)
+            MOE_DEEP_STEP(3)
+        }
+#undef MOE_DEEP_STEP
     }
 
     if (!wave_on) return;
-    const int col = n_wave + frag_row;
 #pragma unroll
-    for (int m = 0; m < kMB; ++m) {
+    for (int i = 0; i < kMBW; ++i) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int r = m * 16 + 4 * (lane >> 4) + q;
+            const int r = (i * C::kWM + wm) * 16 + 4 * (lane >> 4) + q;
             if (r >= M) continue;
-            if (kGated) {  // H row: bf16, the operand of the down pass
-                uint16_t* crow = static_cast<uint16_t*>(Cout) + (row0 + r) * N;
-                const float g = acc[0][m][q], u = acc[1][m][q];
-                crow[col] = f32_to_bf16_bits(g / (1.0f + __expf(-g)) * u);
+            if (kGated) {  // H row: bf16, the operand of the down pass; first half gate blocks, second up
+                uint16_t* crow = static_cast<uint16_t*>(Cout) + (row0 + r) * N + n_wave + frag_row;
+#pragma unroll
+                for (int c = 0; c < kNB / 2; ++c) {
+                    const float g = acc[c][i][q], u = acc[kNB / 2 + c][i][q];
+                    crow[16 * c] = f32_to_bf16_bits(g / (1.0f + __expf(-g)) * u);
+                }
             } else {       // Y row: float32
-                float* crow = static_cast<float*>(Cout) + (row0 + r) * N;
-                crow[col] = acc[0][m][q];
-                crow[col + 16] = acc[1][m][q];
+                float* crow = static_cast<float*>(Cout) + (row0 + r) * N + n_wave + frag_row;
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) crow[16 * b] = acc[b][i][q];
             }
         }
     }
 }
 
-template <bool kGated>
-__global__ __launch_bounds__(kGemmThreads) void grouped_ffn_kernel(
+// One workgroup per CU is the design point (LDS tile and register budget), so the
+// register allocator is told that occupancy is fixed and may spend registers on
+// keeping loads in flight rather than on reaching a higher wave count.
+template <class C, bool kGated>
+__global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, C::kWaves / 4)))
+void grouped_ffn_kernel(
     const uint16_t* __restrict__ A, const int4* __restrict__ tiles, const int32_t* __restrict__ tile_start,
     int E, int n_tiles, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int N, int K,
     void* __restrict__ Cout) {
-    constexpr int kColsW = kGated ? 16 : 32;  // output columns per wave
-    constexpr int kColsWG = kColsW * kGemmWaves;
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * 16 * kMaxRowBlocks * kAStride];
+    constexpr int kColsW = kGated ? C::kWRows / 2 : C::kWRows;  // output columns per wave
+    constexpr int kColsWG = kColsW * C::kWN;
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2 * C::kBufElems];
 
     // ---- work item: (m-tile, n-tile) from the XCD-ordered schedule
     const int n_mt = tile_start[E];
@@ -224,39 +307,77 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_ffn_kernel(
     const int64_t row0 = tile.y;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_wave = nt * kColsWG + wave * kColsW;
+    const int wm = wave % C::kWM, wn = wave / C::kWM;
+    const int n_wave = nt * kColsWG + wn * kColsW;
     const bool wave_on = n_wave < N;  // uniform per wave
     const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
 
-    // weight rows of this lane for the two B blocks (an idle wave reads valid rows it never uses)
+    // weight rows of this lane for the four B blocks (an idle wave reads valid rows it never uses)
     const int n_safe = wave_on ? n_wave : 0;
     const int64_t wexp = static_cast<int64_t>(e) * N * K;
-    const uint16_t* wb0 = W0 + wexp + static_cast<int64_t>(n_safe + frag_row) * K + frag_k;
-    const uint16_t* wb1 = kGated ? W1 + wexp + static_cast<int64_t>(n_safe + frag_row) * K + frag_k
-                                 : W0 + wexp + static_cast<int64_t>(n_safe + 16 + frag_row) * K + frag_k;
+    const uint16_t* w0 = W0 + wexp + static_cast<int64_t>(n_safe + frag_row) * K + frag_k;
+    const uint16_t* w1 = kGated ? W1 + wexp + static_cast<int64_t>(n_safe + frag_row) * K + frag_k : w0;
+    const int64_t blk = 16 * static_cast<int64_t>(K);
+    // gate/up: blocks 0 .. kNB/2-1 are gate rows, the rest the same rows of up
+    const uint16_t* wb[C::kNB];
+#pragma unroll
+    for (int b = 0; b < C::kNB; ++b)
+        wb[b] = kGated ? (b < C::kNB / 2 ? w0 + b * blk : w1 + (b - C::kNB / 2) * blk) : w0 + b * blk;
 
     // one straight-line K loop per row-block count, chosen once per tile
-    if (M <= 32)
-        ffn_tile<kGated, 2>(sA, A, row0, M, wb0, wb1, wave_on, N, K, n_wave, Cout);
-    else if (M <= 64)
-        ffn_tile<kGated, 4>(sA, A, row0, M, wb0, wb1, wave_on, N, K, n_wave, Cout);
-    else
-        ffn_tile<kGated, kMaxRowBlocks>(sA, A, row0, M, wb0, wb1, wave_on, N, K, n_wave, Cout);
+    constexpr int kStepMB = C::kStepMB;
+    const int mb = min(C::kMaxMB, ((M + 16 * kStepMB - 1) / (16 * kStepMB)) * kStepMB);
+#define MOE_TILE(NB)                                                                                   \
+    if (mb == (NB)) {                                                                                  \
+        ffn_tile<C, kGated, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, row0, M, wb, wave_on, N, K, wm, \
+                                                                   n_wave, Cout);                      \
+        return;                                                                                        \
+    }
+    MOE_TILE(kStepMB)
+    MOE_TILE(2 * kStepMB)
+    MOE_TILE(3 * kStepMB)
+    MOE_TILE(4 * kStepMB)
+    MOE_TILE(5 * kStepMB)
+    MOE_TILE(6 * kStepMB)
+    MOE_TILE(7 * kStepMB)
+    MOE_TILE(8 * kStepMB)
+#undef MOE_TILE
 }
 
 // ---------------------------------------------------------------- launchers
 
-int ffn_tile_rows() { return 16 * kMaxRowBlocks; }
-
-int ffn_max_tiles(int64_t n_rows, int E) {
-    const int64_t bm = ffn_tile_rows();
+static int max_tiles_for(int64_t n_rows, int E, int bm) {
     int64_t t = (n_rows + bm - 1) / bm + E;
     if (t > n_rows) t = n_rows;
     if (t < 1) t = 1;
     return static_cast<int>(t);
 }
 
-static int xcd_slots(int max_tiles) { return (max_tiles + kXcds - 1) / kXcds; }
+template <class C, bool kGated>
+hipError_t launch_ffn(const uint16_t* A, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int E,
+                      const uint16_t* W0, const uint16_t* W1, int N, int K, void* Cout, hipStream_t stream) {
+    static_assert(C::kMaxMB <= 8 * C::kStepMB && C::kMaxMB % C::kStepMB == 0,
+                  "the block-count dispatch covers up to 8 steps");
+    const int cols_wg = (kGated ? C::kWRows / 2 : C::kWRows) * C::kWN;
+    const int n_tiles = (N + cols_wg - 1) / cols_wg;
+    const int slots = (max_tiles_for(n_rows, E, C::kBM) + kXcds - 1) / kXcds;
+    const int64_t grid = static_cast<int64_t>(kXcds) * slots * n_tiles;
+    hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
+                       stream, A, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
+    return hipGetLastError();
+}
+
+// 8 waves x 32 weight rows, K step 64, m-tiles of up to 192 rows, LDS rows padded
+// by 32 B (chosen by measurement on the prefill, decode, many-expert and skewed
+// loads: padding by 16 B showed bank conflicts on gfx950, deeper prefetch and
+// 2-D wave grids were slower).
+using GateUpCfg = GemmCfg<1, 8, 2, 64, 12, false, 16>;
+using DownCfg = GemmCfg<1, 8, 2, 64, 12, false, 16>;
+static_assert(GateUpCfg::kBM == DownCfg::kBM, "both passes share one m-tile list");
+
+int ffn_tile_rows() { return GateUpCfg::kBM; }
+
+int ffn_max_tiles(int64_t n_rows, int E) { return max_tiles_for(n_rows, E, ffn_tile_rows()); }
 
 hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int E, int4* tiles,
                               int32_t* tile_start, hipStream_t stream) {
@@ -268,20 +389,12 @@ hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int
 hipError_t launch_gate_up(const uint16_t* x_perm, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
                           int d, int E, int h, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
                           hipStream_t stream) {
-    const int n_tiles = (h + 16 * kGemmWaves - 1) / (16 * kGemmWaves);
-    const int64_t grid = static_cast<int64_t>(kXcds) * xcd_slots(ffn_max_tiles(n_rows, E)) * n_tiles;
-    hipLaunchKernelGGL(grouped_ffn_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads),
-                       0, stream, x_perm, tiles, tile_start, E, n_tiles, w_gate, w_up, h, d, h_act);
-    return hipGetLastError();
+    return launch_ffn<GateUpCfg, true>(x_perm, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act, stream);
 }
 
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream) {
-    const int n_tiles = (d + 32 * kGemmWaves - 1) / (32 * kGemmWaves);
-    const int64_t grid = static_cast<int64_t>(kXcds) * xcd_slots(ffn_max_tiles(n_rows, E)) * n_tiles;
-    hipLaunchKernelGGL(grouped_ffn_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads),
-                       0, stream, h_act, tiles, tile_start, E, n_tiles, w_down, nullptr, d, h, y_rows);
-    return hipGetLastError();
+    return launch_ffn<DownCfg, false>(h_act, tiles, tile_start, n_rows, E, w_down, nullptr, d, h, y_rows, stream);
 }
 
 }  // namespace moe
