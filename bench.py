@@ -5,7 +5,8 @@
 
 A step is one pass of the whole layer over one batch: gate logits + top-k
 (moe_route), grouping by expert (moe_permute), the grouped SwiGLU GEMM
-(moe_expert_gate_up, moe_expert_down) and the weighted combine (moe_combine),
+(moe_expert_gate_up reading x through row_src -- the dispatch gather fused
+into the GEMM -- and moe_expert_down) and the weighted combine (moe_combine),
 enqueued through the C ABI on one stream with buffers allocated beforehand --
 exactly the kernels moe_forward launches, checked bitwise against it below.
 HIP events on that stream time each GEMM pass inside every timed step.
@@ -62,7 +63,6 @@ class Layer:
         self.offsets = e(E + 1, dt=torch.int32)
         self.row_of = e(T, k, dt=torch.int32)
         self.row_src = e(n, dt=torch.int32)
-        self.x_perm = e(n, d, dt=torch.bfloat16)
         self.h_act = e(n, h, dt=torch.bfloat16)
         self.y_rows = e(n, d, dt=torch.float32)
         self.out = e(T, d, dt=torch.float32)
@@ -79,11 +79,11 @@ class Layer:
         L, P, sh, sp, i = self.lib.lib, self.P, self.sh, self.sp, self.inp
         c = self.lib.check
         c(L.moe_route(sh, P(i.x), P(i.w_router), P(i.router_bias), P(self.logits), P(self.idx), P(self.w), sp))
-        c(L.moe_permute(sh, P(i.x), P(self.idx), P(self.offsets), P(self.row_of), P(self.row_src), P(self.x_perm),
+        c(L.moe_permute(sh, None, P(self.idx), P(self.offsets), P(self.row_of), P(self.row_src), None,
                         P(self.ws_perm), self.ws_perm.numel(), sp))
         if ev is not None:
             ev[0].record(self.stream)
-        c(L.moe_expert_gate_up(sh, P(self.x_perm), P(self.offsets), P(i.w_gate), P(i.w_up), P(self.h_act),
+        c(L.moe_expert_gate_up(sh, P(i.x), P(self.row_src), P(self.offsets), P(i.w_gate), P(i.w_up), P(self.h_act),
                                P(self.ws_ffn), self.ws_ffn.numel(), sp))
         if ev is not None:
             ev[1].record(self.stream)
@@ -219,8 +219,9 @@ def main():
     touched = int((counts > 0).sum())
     gemm_flops = 6.0 * n * d * h
     gemm_tflops = gemm_flops / ((gate_up_ms + down_ms) * 1e-3) / 1e12
-    # algorithmic bytes of one gate/up launch: x_perm rows read, touched experts'
-    # gate and up weights read once, H written
+    # algorithmic bytes of one gate/up launch: one bf16 row of x per assignment
+    # (gathered through row_src), touched experts' gate and up weights read once,
+    # H written
     gu_bytes = 2.0 * n * d + 2.0 * 2 * d * h * touched + 2.0 * n * h
     gu_gbs = gu_bytes / (gate_up_ms * 1e-3) / 1e9
     down_bytes = 2.0 * n * h + 2.0 * d * h * touched + 4.0 * n * d

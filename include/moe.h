@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -77,11 +77,11 @@ typedef enum moe_fwd_slot {
     MOE_FWD_EXPERT_OFFSETS = 3, /* int32   [E + 1]  */
     MOE_FWD_ROW_OF = 4,         /* int32   [T, k]   */
     MOE_FWD_ROW_SRC = 5,        /* int32   [T * k]  */
-    MOE_FWD_X_PERM = 6,         /* bf16    [T * k, d] */
-    MOE_FWD_H = 7,              /* bf16    [T * k, h] */
-    MOE_FWD_Y = 8,              /* float   [T * k, d] */
-    MOE_FWD_NUM_SLOTS = 9
+    MOE_FWD_H = 6,              /* bf16    [T * k, h] */
+    MOE_FWD_Y = 7,              /* float   [T * k, d] */
+    MOE_FWD_NUM_SLOTS = 8
 } moe_fwd_slot_t;
+/* moe_forward keeps no x_perm: its gate/up pass reads x through row_src. */
 
 /* Version of this ABI (MOE_ABI_VERSION). */
 int moe_abi_version(void);
@@ -138,14 +138,16 @@ int moe_topk_softmax(const moe_shape_t* shape, const float* logits, int32_t* top
  * moe_permute -- group the T*k (token, slot) assignments by expert, stably, and
  * gather the token rows into expert order (the "grouped by expert" dispatch).
  *
- *  x              [T, d]   bf16  (read)
+ *  x              [T, d]   bf16  (read; may be NULL when x_perm is NULL)
  *  topk_idx       [T, k]   int32 expert of each assignment, in [0, E) (read);
  *                          an id outside [0, E) is skipped: its row_of entry is -1
  *  expert_offsets [E + 1]  int32 out: rows of expert e are expert_offsets[e] ..
  *                          expert_offsets[e+1]-1; expert_offsets[0] = 0
  *  row_of         [T, k]   int32 out: row that holds assignment (t, j)
  *  row_src        [T * k]  int32 out: token of each row
- *  x_perm         [T * k, d] bf16 out: x_perm[r] = x[row_src[r]]
+ *  x_perm         [T * k, d] bf16 out: x_perm[r] = x[row_src[r]]; NULL skips the
+ *                          gather (a caller that passes x and row_src to
+ *                          moe_expert_ffn needs no x_perm)
  *  ws, ws_bytes   workspace of at least moe_workspace_bytes(shape, MOE_CALL_PERMUTE)
  * Within an expert, rows follow the flattened assignment index t*k + j.
  */
@@ -158,7 +160,11 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
  * MFMA with float32 accumulation). "Kimi K3: Open Frontier Intelligence",
  * section "Operational Execution Flow" (SwiGLU-form experts).
  *
- *  x_perm         [T * k, d] bf16 rows grouped by expert (read)
+ *  a, a_rows      the rows grouped by expert (read), given one of two ways:
+ *                 a_rows == NULL: a = x_perm [T * k, d] bf16, row r is a[r];
+ *                 a_rows != NULL: a = x [T, d] bf16 and a_rows = row_src [T * k]
+ *                 int32 from moe_permute, row r is a[a_rows[r]] (the dispatch
+ *                 gather done inside the GEMM; ids are clamped to [0, T))
  *  expert_offsets [E + 1]    int32 as written by moe_permute (read; only the
  *                            device copy is used, the host never sees it)
  *  w_gate, w_up   [E, h, d]  bf16 (read)
@@ -167,20 +173,20 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
  *  y_rows         [T * k, d] float32 out: h_act w_down[e]^T (float32 accumulation)
  *  ws, ws_bytes   workspace of at least moe_workspace_bytes(shape, MOE_CALL_EXPERT_FFN)
  */
-int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm,
+int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
                    const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
                    const uint16_t* w_down, uint16_t* h_act, float* y_rows, void* ws,
                    size_t ws_bytes, void* stream);
 
 /*
  * moe_expert_gate_up -- the first half of moe_expert_ffn on its own:
- * h_act[r] = silu(x_perm[r] w_gate[e]^T) * (x_perm[r] w_up[e]^T) for every row r
- * of expert e, rounded once to bf16. Arguments as in moe_expert_ffn; the
- * workspace is the same size (MOE_CALL_EXPERT_FFN).
+ * h_act[r] = silu(A_r w_gate[e]^T) * (A_r w_up[e]^T) for every row r of expert
+ * e (A_r as in moe_expert_ffn), rounded once to bf16. Arguments as in
+ * moe_expert_ffn; the workspace is the same size (MOE_CALL_EXPERT_FFN).
  */
-int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* x_perm, const int32_t* expert_offsets,
-                       const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, void* ws,
-                       size_t ws_bytes, void* stream);
+int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                       const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                       uint16_t* h_act, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_expert_down -- the second half of moe_expert_ffn on its own:
@@ -202,9 +208,10 @@ int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* ro
                 const float* topk_w, float* out, void* stream);
 
 /*
- * moe_forward -- the whole layer: moe_route, moe_permute, moe_expert_ffn and
- * moe_combine in sequence on one stream, intermediates in the workspace at the
- * offsets moe_forward_ws_offset() gives.
+ * moe_forward -- the whole layer: moe_route, moe_permute (without x_perm),
+ * moe_expert_ffn (reading x through row_src) and moe_combine in sequence on one
+ * stream, intermediates in the workspace at the offsets moe_forward_ws_offset()
+ * gives.
  *
  *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL;
  *  w_gate, w_up [E, h, d] bf16; w_down [E, d, h] bf16 (all read)

@@ -22,7 +22,8 @@ MOE_CALL_PERMUTE = 0
 MOE_CALL_EXPERT_FFN = 1
 MOE_CALL_FORWARD = 2
 
-FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "x_perm", "h_act", "y_rows"]
+FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
+ABI_VERSION = 2
 
 
 class MoeShape(ctypes.Structure):
@@ -51,8 +52,8 @@ def _load():
         "moe_route": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
         "moe_topk_softmax": (ctypes.c_int, [S, P, P, P, P]),
         "moe_permute": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
-        "moe_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
-        "moe_expert_gate_up": (ctypes.c_int, [S, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_expert_gate_up": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_down": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [S, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
@@ -61,6 +62,8 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.moe_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.moe_abi_version()}, this binding needs {ABI_VERSION}")
     return lib
 
 

@@ -164,7 +164,8 @@ __device__ __forceinline__ void mfma_step(f32x4 (&acc)[kNB][kMBW], const uint16_
 // row M - 1 and prefetch indices are clamped to the last K step (a repeated
 // step is loaded but never used).
 template <class C, bool kGated, int kMB>
-__device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restrict__ A, int64_t row0, int M,
+__device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restrict__ A,
+                                         const int32_t* __restrict__ A_rows, int64_t A_nrows, int64_t row0, int M,
                                          const uint16_t* const (&wb)[C::kNB], bool wave_on, int N, int K, int wm,
                                          int n_wave, void* __restrict__ Cout) {
     constexpr int kNB = C::kNB, kSub = C::kSub, kKS = C::kKS;
@@ -178,10 +179,16 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
     const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
 
     const int a_row = tid / kChunks, a_col = 8 * (tid % kChunks);
-    const uint16_t* a_src = A + row0 * K + a_col;
+    // row r of the tile is A[row0 + r], or A[A_rows[row0 + r]] when the rows are
+    // gathered on the fly (the dispatch fused into this pass)
+    const uint16_t* a_src = A + a_col;
     int64_t a_off[kAPasses];
 #pragma unroll
-    for (int p = 0; p < kAPasses; ++p) a_off[p] = static_cast<int64_t>(min(p * kRowsPerPass + a_row, M - 1)) * K;
+    for (int p = 0; p < kAPasses; ++p) {
+        const int64_t r = row0 + min(p * kRowsPerPass + a_row, M - 1);
+        const int64_t src = A_rows ? min(max(static_cast<int64_t>(A_rows[r]), int64_t(0)), A_nrows - 1) : r;
+        a_off[p] = src * K;
+    }
     uint16_t* a_dst[2] = {sA + a_row * C::kAStride + a_col, sA + a_row * C::kAStride + a_col + C::kBufElems};
     const uint16_t* a_frag[2] = {sA + (wm * 16 + frag_row) * C::kAStride + frag_k,
                                  sA + (wm * 16 + frag_row) * C::kAStride + frag_k + C::kBufElems};
@@ -280,9 +287,9 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
 template <class C, bool kGated>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, C::kWaves / 4)))
 void grouped_ffn_kernel(
-    const uint16_t* __restrict__ A, const int4* __restrict__ tiles, const int32_t* __restrict__ tile_start,
-    int E, int n_tiles, const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int N, int K,
-    void* __restrict__ Cout) {
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ A_rows, int64_t A_nrows,
+    const int4* __restrict__ tiles, const int32_t* __restrict__ tile_start, int E, int n_tiles,
+    const uint16_t* __restrict__ W0, const uint16_t* __restrict__ W1, int N, int K, void* __restrict__ Cout) {
     constexpr int kColsW = kGated ? C::kWRows / 2 : C::kWRows;  // output columns per wave
     constexpr int kColsWG = kColsW * C::kWN;
     __shared__ __attribute__((aligned(16))) uint16_t sA[2 * C::kBufElems];
@@ -329,8 +336,8 @@ void grouped_ffn_kernel(
     const int mb = min(C::kMaxMB, ((M + 16 * kStepMB - 1) / (16 * kStepMB)) * kStepMB);
 #define MOE_TILE(NB)                                                                                   \
     if (mb == (NB)) {                                                                                  \
-        ffn_tile<C, kGated, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, row0, M, wb, wave_on, N, K, wm, \
-                                                                   n_wave, Cout);                      \
+        ffn_tile<C, kGated, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, A_rows, A_nrows, row0, M, wb,    \
+                                                                   wave_on, N, K, wm, n_wave, Cout);   \
         return;                                                                                        \
     }
     MOE_TILE(kStepMB)
@@ -354,8 +361,9 @@ static int max_tiles_for(int64_t n_rows, int E, int bm) {
 }
 
 template <class C, bool kGated>
-hipError_t launch_ffn(const uint16_t* A, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int E,
-                      const uint16_t* W0, const uint16_t* W1, int N, int K, void* Cout, hipStream_t stream) {
+hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows, const int4* tiles,
+                      const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* W0, const uint16_t* W1, int N,
+                      int K, void* Cout, hipStream_t stream) {
     static_assert(C::kMaxMB <= 8 * C::kStepMB && C::kMaxMB % C::kStepMB == 0,
                   "the block-count dispatch covers up to 8 steps");
     const int cols_wg = (kGated ? C::kWRows / 2 : C::kWRows) * C::kWN;
@@ -363,7 +371,7 @@ hipError_t launch_ffn(const uint16_t* A, const int4* tiles, const int32_t* tile_
     const int slots = (max_tiles_for(n_rows, E, C::kBM) + kXcds - 1) / kXcds;
     const int64_t grid = static_cast<int64_t>(kXcds) * slots * n_tiles;
     hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
-                       stream, A, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
+                       stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
     return hipGetLastError();
 }
 
@@ -386,15 +394,17 @@ hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int
     return hipGetLastError();
 }
 
-hipError_t launch_gate_up(const uint16_t* x_perm, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
-                          int d, int E, int h, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
-                          hipStream_t stream) {
-    return launch_ffn<GateUpCfg, true>(x_perm, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act, stream);
+hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                          const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,
+                          const uint16_t* w_up, uint16_t* h_act, hipStream_t stream) {
+    return launch_ffn<GateUpCfg, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act,
+                                       stream);
 }
 
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream) {
-    return launch_ffn<DownCfg, false>(h_act, tiles, tile_start, n_rows, E, w_down, nullptr, d, h, y_rows, stream);
+    return launch_ffn<DownCfg, false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
+                                      y_rows, stream);
 }
 
 }  // namespace moe

@@ -22,9 +22,10 @@ int ffn_tile_rows();
 int ffn_max_tiles(int64_t n_rows, int E);
 hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int E, int4* tiles,
                               int32_t* tile_start, hipStream_t stream);
-hipError_t launch_gate_up(const uint16_t* x_perm, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
-                          int d, int E, int h, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
-                          hipStream_t stream);
+// a_rows == nullptr: GEMM row r is a[r] (a = x_perm); else it is a[a_rows[r]] (a = x with a_nrows rows).
+hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                          const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,
+                          const uint16_t* w_up, uint16_t* h_act, hipStream_t stream);
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream);
 

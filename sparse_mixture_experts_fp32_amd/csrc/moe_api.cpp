@@ -105,7 +105,7 @@ void forward_layout(const moe_shape_t* s, size_t off[MOE_FWD_NUM_SLOTS + 3]) {
     const size_t T = static_cast<size_t>(s->T), E = s->E, k = s->k, d = s->d, h = s->h;
     const size_t sizes[MOE_FWD_NUM_SLOTS + 2] = {
         4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k,
-        2 * T * k * d, 2 * T * k * h, 4 * T * k * d, permute_ws(s), ffn_ws(s)};
+        2 * T * k * h, 4 * T * k * d, permute_ws(s), ffn_ws(s)};
     size_t at = 0;
     for (int i = 0; i < MOE_FWD_NUM_SLOTS + 2; ++i) {
         off[i] = at;
@@ -201,11 +201,13 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
         hipError_t err = moe::launch_zero_i32(expert_offsets, shape->E + 1, s);
         return hip_status(err, "expert_offsets clear");
     }
-    MOE_CHECK_PTR(x);
     MOE_CHECK_PTR(topk_idx);
     MOE_CHECK_PTR(row_of);
     MOE_CHECK_PTR(row_src);
-    MOE_CHECK_PTR(x_perm);
+    if (x_perm != nullptr) {  // x is only read by the gather
+        MOE_CHECK_PTR(x);
+        if (!aligned16(x_perm)) return fail(MOE_ERR_INVALID_ARG, "x_perm is not 16-byte aligned");
+    }
     st = check_ws(ws, ws_bytes, permute_ws(shape));
     if (st != MOE_OK) return st;
     hipError_t err = moe::launch_permute(x, topk_idx, shape->T, shape->d, shape->E, shape->k, expert_offsets,
@@ -213,13 +215,14 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
     return hip_status(err, "permute launch");
 }
 
-int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm, const int32_t* expert_offsets,
-                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, uint16_t* h_act,
-                   float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                   const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                   const uint16_t* w_down, uint16_t* h_act, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
-    MOE_CHECK_PTR(x_perm);
+    MOE_CHECK_PTR(a);
+    if (a_rows != nullptr && !aligned16(a_rows)) return fail(MOE_ERR_INVALID_ARG, "a_rows is not 16-byte aligned");
     MOE_CHECK_PTR(expert_offsets);
     MOE_CHECK_PTR(w_gate);
     MOE_CHECK_PTR(w_up);
@@ -233,20 +236,21 @@ int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* x_perm, const int32
     const FfnWs fw = ffn_carve(shape, ws);
     hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x_perm, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_gate, w_up,
-                              h_act, s);
+    err = moe::launch_gate_up(a, a_rows, shape->T, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h,
+                              w_gate, w_up, h_act, s);
     if (err != hipSuccess) return hip_status(err, "gate_up launch");
     err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
     return hip_status(err, "down launch");
 }
 
-int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* x_perm, const int32_t* expert_offsets,
-                       const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, void* ws, size_t ws_bytes,
-                       void* stream) {
+int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                       const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
+                       void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
-    MOE_CHECK_PTR(x_perm);
+    MOE_CHECK_PTR(a);
+    if (a_rows != nullptr && !aligned16(a_rows)) return fail(MOE_ERR_INVALID_ARG, "a_rows is not 16-byte aligned");
     MOE_CHECK_PTR(expert_offsets);
     MOE_CHECK_PTR(w_gate);
     MOE_CHECK_PTR(w_up);
@@ -258,8 +262,8 @@ int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* x_perm, const i
     const FfnWs fw = ffn_carve(shape, ws);
     hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x_perm, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_gate, w_up,
-                              h_act, s);
+    err = moe::launch_gate_up(a, a_rows, shape->T, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h,
+                              w_gate, w_up, h_act, s);
     return hip_status(err, "gate_up launch");
 }
 
@@ -323,7 +327,6 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     int32_t* offsets = static_cast<int32_t*>(at(MOE_FWD_EXPERT_OFFSETS));
     int32_t* row_of = static_cast<int32_t*>(at(MOE_FWD_ROW_OF));
     int32_t* row_src = static_cast<int32_t*>(at(MOE_FWD_ROW_SRC));
-    uint16_t* x_perm = static_cast<uint16_t*>(at(MOE_FWD_X_PERM));
     uint16_t* h_act = static_cast<uint16_t*>(at(MOE_FWD_H));
     float* y_rows = static_cast<float*>(at(MOE_FWD_Y));
     int32_t* count_ws = static_cast<int32_t*>(at(MOE_FWD_NUM_SLOTS));
@@ -336,11 +339,12 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     if (err != hipSuccess) return hip_status(err, "router_gemm launch");
     err = moe::launch_topk_softmax(logits, T, E, k, idx, w, s);
     if (err != hipSuccess) return hip_status(err, "topk_softmax launch");
-    err = moe::launch_permute(x, idx, T, d, E, k, offsets, row_of, row_src, x_perm, count_ws, s);
+    // the dispatch gather is fused into the gate/up pass: it reads x through row_src
+    err = moe::launch_permute(x, idx, T, d, E, k, offsets, row_of, row_src, nullptr, count_ws, s);
     if (err != hipSuccess) return hip_status(err, "permute launch");
     err = moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x_perm, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s);
+    err = moe::launch_gate_up(x, row_src, T, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s);
     if (err != hipSuccess) return hip_status(err, "gate_up launch");
     err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, d, E, h, w_down, y_rows, s);
     if (err != hipSuccess) return hip_status(err, "down launch");

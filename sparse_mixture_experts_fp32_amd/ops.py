@@ -88,8 +88,9 @@ def moe_topk_softmax(logits, k: int):
     return idx, w
 
 
-def moe_permute(x, topk_idx, E: int):
-    """expert_offsets [E+1], row_of [T,k], row_src [T*k] (int32) and x_perm [T*k, d] bf16."""
+def moe_permute(x, topk_idx, E: int, gather: bool = True):
+    """expert_offsets [E+1], row_of [T,k], row_src [T*k] (int32) and x_perm [T*k, d] bf16
+    (x_perm is None when gather=False: moe_expert_ffn can read x through row_src instead)."""
     _need(x, "x", "bf16")
     dev = x.device
     T, d = x.shape
@@ -99,7 +100,7 @@ def moe_permute(x, topk_idx, E: int):
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     row_of = torch.empty((T, k), dtype=torch.int32, device=dev)
     row_src = torch.empty(T * k, dtype=torch.int32, device=dev)
-    x_perm = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev)
+    x_perm = torch.empty((T * k, d), dtype=torch.bfloat16, device=dev) if gather else None
     ws = workspace(s, _lib.MOE_CALL_PERMUTE, dev)
     with torch.cuda.device(dev):
         _lib.check(_lib.lib.moe_permute(ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(offsets), _ptr(row_of),
@@ -107,13 +108,27 @@ def moe_permute(x, topk_idx, E: int):
     return offsets, row_of, row_src, x_perm
 
 
-def moe_expert_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int):
-    """h_act [T*k, h] bf16 and y_rows [T*k, d] f32 for rows grouped by expert."""
-    _need(x_perm, "x_perm", "bf16")
-    dev = x_perm.device
-    n, d = x_perm.shape
-    if n != T * k:
-        raise ValueError(f"x_perm has {n} rows, expected T*k = {T * k}")
+def _rows_operand(a, a_rows, T, k):
+    """Validate the A operand of the grouped GEMM: x_perm [T*k, d], or x [T, d] with row_src [T*k]."""
+    _need(a, "a", "bf16")
+    dev = a.device
+    n, d = a.shape
+    if a_rows is None:
+        if n != T * k:
+            raise ValueError(f"x_perm has {n} rows, expected T*k = {T * k}")
+    else:
+        if n != T:
+            raise ValueError(f"x has {n} rows, expected T = {T}")
+        _need(a_rows, "a_rows", "i32", (T * k,), dev)
+    return dev, d
+
+
+def moe_expert_ffn(a, expert_offsets, w_gate, w_up, w_down, T: int, k: int, a_rows=None):
+    """h_act [T*k, h] bf16 and y_rows [T*k, d] f32 for rows grouped by expert.
+
+    The rows are a = x_perm [T*k, d] (a_rows None), or a = x [T, d] read through a_rows = row_src [T*k]."""
+    dev, d = _rows_operand(a, a_rows, T, k)
+    n = T * k
     E, h, _ = w_gate.shape
     _need(expert_offsets, "expert_offsets", "i32", (E + 1,), dev)
     _need(w_gate, "w_gate", "bf16", (E, h, d), dev)
@@ -124,9 +139,9 @@ def moe_expert_ffn(x_perm, expert_offsets, w_gate, w_up, w_down, T: int, k: int)
     y_rows = torch.empty((n, d), dtype=torch.float32, device=dev)
     ws = workspace(s, _lib.MOE_CALL_EXPERT_FFN, dev)
     with torch.cuda.device(dev):
-        _lib.check(_lib.lib.moe_expert_ffn(ctypes.byref(s), _ptr(x_perm), _ptr(expert_offsets), _ptr(w_gate),
-                                           _ptr(w_up), _ptr(w_down), _ptr(h_act), _ptr(y_rows), _ptr(ws),
-                                           ws.numel(), _stream(dev)))
+        _lib.check(_lib.lib.moe_expert_ffn(ctypes.byref(s), _ptr(a), _ptr(a_rows), _ptr(expert_offsets),
+                                           _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(h_act), _ptr(y_rows),
+                                           _ptr(ws), ws.numel(), _stream(dev)))
     return h_act, y_rows
 
 
@@ -182,7 +197,7 @@ class MoEForward:
             "logits": (torch.float32, (T, E)), "topk_idx": (torch.int32, (T, k)),
             "topk_w": (torch.float32, (T, k)), "expert_offsets": (torch.int32, (E + 1,)),
             "row_of": (torch.int32, (T, k)), "row_src": (torch.int32, (T * k,)),
-            "x_perm": (torch.bfloat16, (T * k, d)), "h_act": (torch.bfloat16, (T * k, h)),
+            "h_act": (torch.bfloat16, (T * k, h)),
             "y_rows": (torch.float32, (T * k, d)),
         }
         dtype, shp = spec[name]

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == lib.ABI_VERSION == 2
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -92,7 +92,13 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert L.moe_route(ctypes.byref(s), a, a, mis, a, a, a, None) == 1
     assert L.moe_topk_softmax(ctypes.byref(s), None, a, a, None) == 1
     assert L.moe_combine(ctypes.byref(s), a, a, None, a, None) == 1
-    assert L.moe_expert_ffn(ctypes.byref(s), a, a, a, a, None, a, a, a, 1 << 20, None) == 1
+    assert L.moe_expert_ffn(ctypes.byref(s), a, None, a, a, a, None, a, a, a, 1 << 20, None) == 1
+    assert L.moe_expert_ffn(ctypes.byref(s), None, a, a, a, a, a, a, a, a, 1 << 20, None) == 1
+    assert L.moe_expert_ffn(ctypes.byref(s), a, mis, a, a, a, a, a, a, a, 1 << 20, None) == 1
+    assert L.moe_expert_gate_up(ctypes.byref(s), a, None, a, a, None, a, a, 1 << 20, None) == 1
+    # moe_permute: x_perm may be NULL (no gather; x is then not needed), but not misaligned
+    assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, mis, a, 1 << 20, None) == 1
+    assert L.moe_permute(ctypes.byref(s), None, a, a, a, a, a, a, 1 << 20, None) == 1
     assert L.moe_forward(ctypes.byref(s), a, a, None, a, a, a, None, a, 1 << 30, None) == 1
     assert L.moe_route(None, a, a, None, a, a, a, None) == 1
 
@@ -109,7 +115,7 @@ def test_workspace_checks(lib):
     assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, None, need_p, None) == 3
     assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, a, need_p - 1, None) == 3
     assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, ctypes.c_void_p(4096 + 16), need_p, None) == 3
-    assert L.moe_expert_ffn(ctypes.byref(s), a, a, a, a, a, a, a, a, need_f - 1, None) == 3
+    assert L.moe_expert_ffn(ctypes.byref(s), a, None, a, a, a, a, a, a, a, need_f - 1, None) == 3
     assert L.moe_forward(ctypes.byref(s), a, a, None, a, a, a, a, a, need_fw - 256, None) == 3
     assert L.moe_workspace_bytes(ctypes.byref(s), 7) == 0
 
@@ -121,16 +127,17 @@ def test_forward_workspace_layout(lib):
         s = lib.shape(cfg["T"], cfg["d"], cfg["E"], cfg["k"], cfg["h"])
         total = lib.workspace_bytes(s, lib.MOE_CALL_FORWARD)
         T, d, E, k, h = (cfg[c] for c in "TdEkh")
-        sizes = [4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k, 2 * T * k * d, 2 * T * k * h,
-                 4 * T * k * d]
-        offs = [lib.forward_ws_offset(s, i) for i in range(9)]
-        for i in range(9):
+        sizes = [4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k, 2 * T * k * h, 4 * T * k * d]
+        ns = len(lib.FWD_SLOTS)
+        assert ns == len(sizes)
+        offs = [lib.forward_ws_offset(s, i) for i in range(ns)]
+        for i in range(ns):
             assert offs[i] % 256 == 0
             assert offs[i] + sizes[i] <= total
-            if i + 1 < 9:
+            if i + 1 < ns:
                 assert offs[i] + sizes[i] <= offs[i + 1]
     with pytest.raises(lib.MoEError):
-        lib.forward_ws_offset(lib.shape(64, 128, 8, 2, 256), 9)
+        lib.forward_ws_offset(lib.shape(64, 128, 8, 2, 256), len(lib.FWD_SLOTS))
 
 
 def test_zero_tokens_is_a_noop(lib):
@@ -139,4 +146,4 @@ def test_zero_tokens_is_a_noop(lib):
     assert L.moe_route(ctypes.byref(s), None, None, None, None, None, None, None) == 0
     assert L.moe_combine(ctypes.byref(s), None, None, None, None, None) == 0
     assert L.moe_forward(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None) == 0
-    assert L.moe_expert_ffn(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.moe_expert_ffn(ctypes.byref(s), None, None, None, None, None, None, None, None, None, 0, None) == 0

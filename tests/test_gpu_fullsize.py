@@ -47,10 +47,14 @@ def test_full_size_layer(moe, name):
     counts = np.diff(off)
     print(f"[full-size] rows per expert: max {counts.max()}, mean {counts.mean():.1f}, "
           f"empty {(counts == 0).sum()} of {cfg.E}", flush=True)
+    # the standalone dispatch gather on the forward pass's routing: sampled rows of x_perm
     n = cfg.T * cfg.k
     xr = rng.choice(n, size=min(512, n), replace=False)
-    xp = fwd.intermediate("x_perm")
+    _, _, rs2, xp = moe.moe_permute(inp.x, fwd.intermediate("topk_idx"), cfg.E)
+    torch.cuda.synchronize()
+    assert torch.equal(rs2.cpu(), torch.from_numpy(row_src.astype(np.int32)))
     assert torch.equal(xp[torch.from_numpy(xr).to(dev)].cpu(), x_h[torch.from_numpy(row_src[xr])])
+    del xp, rs2
 
     # every H / Y row of two experts (at most 512 sampled rows of a very large one)
     nonempty = np.flatnonzero(counts)
@@ -72,5 +76,5 @@ def test_full_size_layer(moe, name):
                       gu.LazyExperts(inp.w_down), cfg.k, logits=logits[toks])
     max_rel, mean_abs = gu.check_layer(out[torch.from_numpy(toks).to(dev)].cpu(), ref["out"])
     print(f"[full-size] {name}: sampled out max rel {max_rel:.2e}, mean abs {mean_abs:.2e}", flush=True)
-    del fwd, out, inp, xp
+    del fwd, out, inp
     torch.cuda.empty_cache()

@@ -180,15 +180,24 @@ FFN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("gathered", [False, True], ids=["x_perm", "x_row_src"])
 @pytest.mark.parametrize("T,d,E,k,h,skew", FFN_CASES)
-def test_expert_ffn_vs_oracle(dev, moe, T, d, E, k, h, skew):
+def test_expert_ffn_vs_oracle(dev, moe, T, d, E, k, h, skew, gathered):
     cfg = scaled_config("tiny", T=T, d=d, E=E, k=k, h=h, seed=T + d)
     inp = make_inputs(cfg)
     idx = _random_idx(T, E, k, seed=T, skew=skew)
     off, row_of, row_src = orc.permute(idx, E)
     x_perm = inp.x[torch.from_numpy(row_src)]
-    h_act, y_rows = moe.moe_expert_ffn(x_perm.to(dev), torch.from_numpy(off.astype(np.int32)).to(dev),
-                                       inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev), T, k)
+    off_d = torch.from_numpy(off.astype(np.int32)).to(dev)
+    w = (inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev))
+    if gathered:  # rows read from x through row_src inside the GEMM
+        h_act, y_rows = moe.moe_expert_ffn(inp.x.to(dev), off_d, *w, T, k,
+                                           a_rows=torch.from_numpy(row_src.astype(np.int32)).to(dev))
+        h_ref, y_ref = moe.moe_expert_ffn(x_perm.to(dev), off_d, *w, T, k)
+        _sync()
+        assert torch.equal(h_act, h_ref) and torch.equal(y_rows, y_ref), "gathered rows differ from x_perm rows"
+    else:
+        h_act, y_rows = moe.moe_expert_ffn(x_perm.to(dev), off_d, *w, T, k)
     _sync()
     H_ref, Y_ref = orc.expert_ffn(x_perm, off, inp.w_gate, inp.w_up, inp.w_down)
     hg, yg = h_act.cpu(), y_rows.cpu()
@@ -253,16 +262,19 @@ def test_forward_vs_oracle(dev, moe, base, over):
     gu.check_route(fwd.intermediate("logits"), fwd.intermediate("topk_idx"), fwd.intermediate("topk_w"), cfg.k)
     gu.check_permutation(fwd.intermediate("expert_offsets"), fwd.intermediate("row_of"),
                          fwd.intermediate("row_src"), ref["idx"], cfg.E)
-    assert torch.equal(fwd.intermediate("x_perm").cpu(), inp.x[torch.from_numpy(ref["row_src"])])
     gu.check_layer(out, ref["out"])
-    # the forward pass equals the four calls made one by one
+    # the forward pass (gather fused into the gate/up pass) equals the four calls
+    # made one by one with an explicit x_perm, bit for bit
     g = inp.to(dev)
     logits, idx, w = moe.moe_route(g.x, g.w_router, g.router_bias, cfg.k)
     off, row_of, row_src, x_perm = moe.moe_permute(g.x, idx, cfg.E)
+    _sync()
+    assert torch.equal(x_perm.cpu(), inp.x[torch.from_numpy(ref["row_src"])])
     h_act, y_rows = moe.moe_expert_ffn(x_perm, off, g.w_gate, g.w_up, g.w_down, cfg.T, cfg.k)
     out2 = moe.moe_combine(y_rows, row_of, w)
     _sync()
     assert torch.equal(out2, out)
+    assert torch.equal(h_act, fwd.intermediate("h_act"))
 
 
 def test_forward_identical_experts_is_dense_ffn(dev, moe):
