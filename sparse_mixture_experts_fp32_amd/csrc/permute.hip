@@ -1,105 +1,160 @@
 // Grouping the (token, slot) assignments by expert: per-chunk histograms, one
 // prefix scan, then a stable rank within each chunk, and the row gather.
 //
-// The assignments a = t * k + j are cut into chunks of `chunk` consecutive
-// indices. Rows of expert e are ordered by a, so the first row of chunk c
-// inside expert e is
+// The assignments a = t * k + j are cut into at most kMaxChunks chunks of
+// consecutive indices. Rows of expert e are ordered by a, so the first row of
+// chunk c inside expert e is
 //     offsets[e] + sum_{c' < c} count[e, c'],
-// i.e. an exclusive scan of count laid out expert-major, chunk-minor. Inside a
-// chunk, one wavefront walks the assignments in order, 64 at a time, and ranks
-// equal experts within the 64 lanes with ballots (no atomics on the order), so
-// the permutation is exact and deterministic. Per-expert token counts never
-// leave the device ("Kimi K3: Open Frontier Intelligence", section "Systems
-// Optimization, Load Balancing, and Post-Training Alignment": waiting on dynamic
-// counts on the host stalls the device).
+// an exclusive scan of count laid out expert-major, chunk-minor. A chunk is
+// handled by one workgroup of kRankWaves wavefronts, each owning a contiguous
+// slice of the chunk and walking it 64 assignments at a time in order.
+//
+// Equal experts among the 64 lanes are found without atomics and without a
+// loop over distinct experts: one ballot per bit of the expert id gives every
+// lane the mask of lanes holding the same id (AND of the ballots where its bit
+// is set and of the complements where it is clear). The lane's rank among
+// them is a popcount of the lower lanes in that mask, and only the lowest such
+// lane updates the expert's counter, so the result is exact and deterministic.
+// Per-expert token counts never leave the device ("Kimi K3: Open Frontier
+// Intelligence", section "Systems Optimization, Load Balancing, and
+// Post-Training Alignment": waiting on dynamic counts on the host stalls the
+// device).
 #include "device_common.h"
 #include "launch.h"
 
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
+constexpr int kMaxChunks = 32;
+constexpr int kRankWaves = 8;
 
-// count[e * nchunks + c] = number of assignments of chunk c that chose expert e.
-__global__ __launch_bounds__(256) void expert_count_kernel(const int32_t* __restrict__ topk_idx,
-                                                           int64_t n_assign, int E, int chunk,
-                                                           int nchunks, int32_t* __restrict__ count) {
-    __shared__ int32_t hist[kMaxExperts];
-    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-    __syncthreads();
-    const int c = blockIdx.x;
-    const int64_t lo = static_cast<int64_t>(c) * chunk;
-    const int64_t hi = min(lo + chunk, n_assign);
-    for (int64_t a = lo + threadIdx.x; a < hi; a += blockDim.x) {
-        const int e = topk_idx[a];
-        if (e >= 0 && e < E) atomicAdd(&hist[e], 1);  // integer counts: order-independent
+// Mask of the lanes whose key equals this lane's key (keys below 2^nbits).
+__device__ __forceinline__ uint64_t same_key_lanes(uint32_t key, int nbits, uint64_t active) {
+    uint64_t same = active;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t m = __ballot(bit);
+        same &= bit ? m : ~m;
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) count[static_cast<int64_t>(e) * nchunks + c] = hist[e];
+    return same;
 }
 
-// In-place exclusive scan of count[0 .. E*nchunks) by one 1024-thread workgroup;
-// also writes expert_offsets[e] = scanned value of (e, chunk 0) and the total.
+// Assignment slice [lo, hi) of wave w inside chunk c (slices are multiples of 64).
+__device__ __forceinline__ void wave_slice(int64_t n_assign, int chunk, int c, int w, int64_t& lo, int64_t& hi) {
+    const int64_t c0 = static_cast<int64_t>(c) * chunk;
+    const int64_t c1 = min(c0 + chunk, n_assign);
+    const int64_t per = ((c1 - c0 + kRankWaves * 64 - 1) / (kRankWaves * 64)) * 64;
+    lo = min(c0 + w * per, c1);
+    hi = min(lo + per, c1);
+}
+
+// Adds the expert histogram of this wave's slice to hist[0 .. E) (hist private to the wave).
+__device__ void wave_histogram(const int32_t* __restrict__ topk_idx, int64_t lo, int64_t hi, int E, int nbits,
+                               int32_t* hist) {
+    const int lane = threadIdx.x & 63;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t a0 = lo; a0 < hi; a0 += 64) {
+        const int64_t a = a0 + lane;
+        const bool in = a < hi;
+        const int e = in ? topk_idx[a] : -1;
+        const bool valid = in && e >= 0 && e < E;
+        const uint32_t key = valid ? static_cast<uint32_t>(e) : (1u << nbits) - 1u;
+        const uint64_t same = same_key_lanes(key, nbits, __ballot(valid));
+        if (valid && (same & below) == 0) hist[e] += __popcll(same);
+    }
+}
+
+// count[e * nchunks + c] = assignments of chunk c that chose expert e.
+__global__ __launch_bounds__(kRankWaves * 64) void expert_count_kernel(const int32_t* __restrict__ topk_idx,
+                                                                       int64_t n_assign, int E, int nbits, int chunk,
+                                                                       int nchunks, int32_t* __restrict__ count) {
+    __shared__ int32_t hist[kRankWaves][kMaxExperts];
+    const int w = threadIdx.x >> 6, c = blockIdx.x;
+    for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) hist[i / E][i % E] = 0;
+    __syncthreads();
+    int64_t lo, hi;
+    wave_slice(n_assign, chunk, c, w, lo, hi);
+    wave_histogram(topk_idx, lo, hi, E, nbits, hist[w]);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int32_t s = 0;
+#pragma unroll
+        for (int v = 0; v < kRankWaves; ++v) s += hist[v][e];
+        count[static_cast<int64_t>(e) * nchunks + c] = s;
+    }
+}
+
+// One 1024-thread workgroup; thread e owns expert e's nchunks (<= kMaxChunks) counts.
+// Rewrites count[e, c] as the first row of (e, c); expert_offsets[e] = first row of e.
 __global__ __launch_bounds__(1024) void expert_scan_kernel(int32_t* __restrict__ count, int E, int nchunks,
                                                            int32_t* __restrict__ expert_offsets) {
     __shared__ int32_t part[1024];
-    const int64_t n = static_cast<int64_t>(E) * nchunks;
     const int tid = threadIdx.x;
-    const int64_t per = (n + 1023) / 1024;
-    const int64_t lo = min(n, tid * per), hi = min(n, lo + per);
-    int32_t s = 0;
-    for (int64_t i = lo; i < hi; ++i) s += count[i];
-    part[tid] = s;
+    int32_t cnt[kMaxChunks];
+    int32_t total = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+        cnt[c] = (tid < E && c < nchunks) ? count[static_cast<int64_t>(tid) * nchunks + c] : 0;
+        total += cnt[c];
+    }
+    part[tid] = total;
     __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 partial sums
-    for (int off = 1; off < 1024; off <<= 1) {
+    for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
         const int32_t v = tid >= off ? part[tid - off] : 0;
         __syncthreads();
         part[tid] += v;
         __syncthreads();
     }
-    int32_t run = part[tid] - s;  // exclusive prefix of this thread's segment
-    for (int64_t i = lo; i < hi; ++i) {
-        const int32_t v = count[i];
-        count[i] = run;
-        if (i % nchunks == 0) expert_offsets[i / nchunks] = run;
-        run += v;
+    int32_t run = part[tid] - total;
+    if (tid < E) {
+        expert_offsets[tid] = run;
+#pragma unroll
+        for (int c = 0; c < kMaxChunks; ++c) {
+            if (c < nchunks) count[static_cast<int64_t>(tid) * nchunks + c] = run;
+            run += cnt[c];
+        }
     }
     if (tid == 1023) expert_offsets[E] = part[1023];
 }
 
-// One wavefront per chunk: stable ranks, row_of and row_src.
-__global__ __launch_bounds__(64) void expert_rank_kernel(const int32_t* __restrict__ topk_idx,
-                                                         int64_t n_assign, int k, int E, int chunk,
-                                                         int nchunks, const int32_t* __restrict__ base,
-                                                         int32_t* __restrict__ row_of,
-                                                         int32_t* __restrict__ row_src) {
-    __shared__ int32_t next[kMaxExperts];
-    const int lane = threadIdx.x;
-    const int c = blockIdx.x;
-    for (int e = lane; e < E; e += 64) next[e] = base[static_cast<int64_t>(e) * nchunks + c];
+// One workgroup per chunk: stable ranks, row_of and row_src.
+__global__ __launch_bounds__(kRankWaves * 64) void expert_rank_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t n_assign, int k, int E, int nbits, int chunk, int nchunks,
+    const int32_t* __restrict__ base, int32_t* __restrict__ row_of, int32_t* __restrict__ row_src) {
+    __shared__ int32_t next[kRankWaves][kMaxExperts];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = blockIdx.x;
+    for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) next[i / E][i % E] = 0;
     __syncthreads();
-    const int64_t lo = static_cast<int64_t>(c) * chunk;
-    const int64_t hi = min(lo + chunk, n_assign);
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int64_t lo, hi;
+    wave_slice(n_assign, chunk, c, w, lo, hi);
+    wave_histogram(topk_idx, lo, hi, E, nbits, next[w]);
+    __syncthreads();
+    // first row of (expert e, wave v) = chunk base + assignments of e in waves < v
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+        int32_t run = base[static_cast<int64_t>(e) * nchunks + c];
+#pragma unroll
+        for (int v = 0; v < kRankWaves; ++v) {
+            const int32_t n = next[v][e];
+            next[v][e] = run;
+            run += n;
+        }
+    }
+    __syncthreads();
+    int32_t* nx = next[w];
+    const uint64_t below = (1ull << lane) - 1ull;
     for (int64_t a0 = lo; a0 < hi; a0 += 64) {
         const int64_t a = a0 + lane;
-        int e = (a < hi) ? topk_idx[a] : -1;
-        const bool valid = (e >= 0 && e < E);
-        if (!valid) e = -1;
+        const bool in = a < hi;
+        const int e = in ? topk_idx[a] : -1;
+        const bool valid = in && e >= 0 && e < E;
+        const uint32_t key = valid ? static_cast<uint32_t>(e) : (1u << nbits) - 1u;
+        const uint64_t same = same_key_lanes(key, nbits, __ballot(valid));
         int pos = -1;
-        uint64_t pending = __ballot(valid);
-        while (pending) {
-            const int leader = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-            const int el = __shfl(e, leader, 64);
-            const uint64_t same = __ballot(e == el);
-            const int b = next[el];
-            if (e == el) pos = b + __popcll(same & below);
-            __syncthreads();  // every lane has read next[el] before the leader moves it
-            if (lane == leader) next[el] = b + __popcll(same);
-            __syncthreads();
-            pending &= ~same;
-        }
-        if (a < hi) {
+        if (valid) pos = nx[e] + static_cast<int>(__popcll(same & below));
+        // every lane has read nx[e] (one LDS instruction, in program order) before the
+        // lowest lane of each expert moves that expert's counter
+        if (valid && (same & below) == 0) nx[e] += static_cast<int>(__popcll(same));
+        if (in) {
             row_of[a] = pos;
             if (pos >= 0) row_src[pos] = static_cast<int32_t>(a / k);
         }
@@ -134,15 +189,24 @@ hipError_t launch_zero_i32(int32_t* p, int n, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Chunk length: a multiple of kRankWaves * 64, at least that, so that there are
+// at most kMaxChunks chunks.
 int permute_chunk(int64_t n_assign) {
-    int64_t c = (n_assign + 255) / 256;  // at most 256 chunks
-    c = (c + 63) / 64 * 64;
-    return static_cast<int>(c < 256 ? 256 : c);
+    const int64_t unit = kRankWaves * 64;
+    const int64_t per = (n_assign + kMaxChunks - 1) / kMaxChunks;
+    const int64_t c = (per + unit - 1) / unit * unit;
+    return static_cast<int>(c < unit ? unit : c);
 }
 
 int permute_nchunks(int64_t n_assign) {
     const int c = permute_chunk(n_assign);
     return static_cast<int>((n_assign + c - 1) / c);
+}
+
+static int id_bits(int E) {  // bits of the ids 0 .. E (E itself marks "no expert")
+    int b = 1;
+    while ((1 << b) <= E) ++b;
+    return b;
 }
 
 hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T, int d, int E, int k,
@@ -151,12 +215,12 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
     const int64_t n = T * k;
     const int chunk = permute_chunk(n);
     const int nchunks = permute_nchunks(n);
-    hipLaunchKernelGGL(expert_count_kernel, dim3(nchunks), dim3(256), 0, stream, topk_idx, n, E, chunk,
-                       nchunks, count_ws);
-    hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, stream, count_ws, E, nchunks,
-                       expert_offsets);
-    hipLaunchKernelGGL(expert_rank_kernel, dim3(nchunks), dim3(64), 0, stream, topk_idx, n, k, E, chunk,
-                       nchunks, count_ws, row_of, row_src);
+    const int nbits = id_bits(E);
+    hipLaunchKernelGGL(expert_count_kernel, dim3(nchunks), dim3(kRankWaves * 64), 0, stream, topk_idx, n, E, nbits,
+                       chunk, nchunks, count_ws);
+    hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, stream, count_ws, E, nchunks, expert_offsets);
+    hipLaunchKernelGGL(expert_rank_kernel, dim3(nchunks), dim3(kRankWaves * 64), 0, stream, topk_idx, n, k, E, nbits,
+                       chunk, nchunks, count_ws, row_of, row_src);
     if (x_perm != nullptr)
         hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, stream,
                            x, T, d, row_src, expert_offsets + E, n, x_perm);
