@@ -67,6 +67,7 @@ class Layer:
         self.y_rows = e(n, d, dt=torch.float32)
         self.out = e(T, d, dt=torch.float32)
         self.shape = lib.shape(T, d, E, k, h)
+        self.ws_route = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_ROUTE)), dt=torch.uint8)
         self.ws_perm = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_PERMUTE)), dt=torch.uint8)
         self.ws_ffn = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_EXPERT_FFN)), dt=torch.uint8)
         self.stream = torch.cuda.current_stream(dev)
@@ -78,7 +79,8 @@ class Layer:
     def step(self, ev=None):
         L, P, sh, sp, i = self.lib.lib, self.P, self.sh, self.sp, self.inp
         c = self.lib.check
-        c(L.moe_route(sh, P(i.x), P(i.w_router), P(i.router_bias), P(self.logits), P(self.idx), P(self.w), sp))
+        c(L.moe_route(sh, P(i.x), P(i.w_router), P(i.router_bias), P(self.logits), P(self.idx), P(self.w),
+                      P(self.ws_route), self.ws_route.numel(), sp))
         c(L.moe_permute(sh, None, P(self.idx), P(self.offsets), P(self.row_of), P(self.row_src), None,
                         P(self.ws_perm), self.ws_perm.numel(), sp))
         if ev is not None:

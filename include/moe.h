@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -66,7 +66,8 @@ typedef enum moe_status {
 typedef enum moe_call {
     MOE_CALL_PERMUTE = 0,
     MOE_CALL_EXPERT_FFN = 1,
-    MOE_CALL_FORWARD = 2
+    MOE_CALL_FORWARD = 2,
+    MOE_CALL_ROUTE = 3
 } moe_call_t;
 
 /* Intermediates that moe_forward keeps in its workspace (see moe_forward_ws_offset). */
@@ -115,12 +116,14 @@ int moe_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset);
  *                      equal logits (and -0.0 vs +0.0) go to the lower expert id
  *  topk_w      [T, k]  float32 out: softmax probabilities of the selected experts,
  *                      renormalised to sum to 1 (exp(l_j - l_0) / sum_i exp(l_i - l_0))
+ *  ws, ws_bytes        workspace of at least moe_workspace_bytes(shape, MOE_CALL_ROUTE)
+ *                      (w_router split exactly into three bf16 parts for the matrix cores)
  * NaN logits are outside the contract; the ids written are still k distinct
  * experts in [0, E).
  */
 int moe_route(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
               const float* router_bias, float* logits, int32_t* topk_idx, float* topk_w,
-              void* stream);
+              void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_topk_softmax -- the second half of moe_route on caller-supplied float32

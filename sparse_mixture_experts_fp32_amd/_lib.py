@@ -21,9 +21,10 @@ MOE_ERR_HIP = 4
 MOE_CALL_PERMUTE = 0
 MOE_CALL_EXPERT_FFN = 1
 MOE_CALL_FORWARD = 2
+MOE_CALL_ROUTE = 3
 
 FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class MoeShape(ctypes.Structure):
@@ -49,7 +50,7 @@ def _load():
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_workspace_bytes": (ctypes.c_size_t, [S, ctypes.c_int]),
         "moe_forward_ws_offset": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
-        "moe_route": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
+        "moe_route": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_topk_softmax": (ctypes.c_int, [S, P, P, P, P]),
         "moe_permute": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),

@@ -78,6 +78,11 @@ size_t permute_ws(const moe_shape_t* s) {
     return align_up(sizeof(int32_t) * static_cast<size_t>(s->E) * moe::permute_nchunks(n));
 }
 
+size_t route_ws(const moe_shape_t* s) {
+    if (s->T == 0) return 0;
+    return align_up(moe::router_parts_bytes(s->d, s->E));
+}
+
 // The grouped GEMM's workspace: the m-tile list, then each expert's first m-tile index.
 size_t ffn_tiles_bytes(const moe_shape_t* s) {
     return align_up(sizeof(int4) * static_cast<size_t>(moe::ffn_max_tiles(s->T * s->k, s->E)));
@@ -99,19 +104,23 @@ FfnWs ffn_carve(const moe_shape_t* s, void* ws) {
     return FfnWs{reinterpret_cast<int4*>(b), reinterpret_cast<int32_t*>(b + ffn_tiles_bytes(s))};
 }
 
-// Byte offsets of every slot of moe_forward's workspace; slot MOE_FWD_NUM_SLOTS
-// holds the permute scratch, the one after it the tile list, then the total.
-void forward_layout(const moe_shape_t* s, size_t off[MOE_FWD_NUM_SLOTS + 3]) {
+// Byte offsets of every slot of moe_forward's workspace; after the public slots
+// come the permute scratch, the tile list and the router's weight parts, then
+// the total.
+constexpr int kFwdPermuteWs = MOE_FWD_NUM_SLOTS, kFwdFfnWs = MOE_FWD_NUM_SLOTS + 1,
+              kFwdRouteWs = MOE_FWD_NUM_SLOTS + 2, kFwdTotal = MOE_FWD_NUM_SLOTS + 3;
+
+void forward_layout(const moe_shape_t* s, size_t off[kFwdTotal + 1]) {
     const size_t T = static_cast<size_t>(s->T), E = s->E, k = s->k, d = s->d, h = s->h;
-    const size_t sizes[MOE_FWD_NUM_SLOTS + 2] = {
+    const size_t sizes[kFwdTotal] = {
         4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k,
-        2 * T * k * h, 4 * T * k * d, permute_ws(s), ffn_ws(s)};
+        2 * T * k * h, 4 * T * k * d, permute_ws(s), ffn_ws(s), route_ws(s)};
     size_t at = 0;
-    for (int i = 0; i < MOE_FWD_NUM_SLOTS + 2; ++i) {
+    for (int i = 0; i < kFwdTotal; ++i) {
         off[i] = at;
         at += align_up(sizes[i]);
     }
-    off[MOE_FWD_NUM_SLOTS + 2] = at;
+    off[kFwdTotal] = at;
 }
 
 }  // namespace
@@ -138,11 +147,12 @@ size_t moe_workspace_bytes(const moe_shape_t* shape, int call) {
     switch (call) {
         case MOE_CALL_PERMUTE: ok(); return permute_ws(shape);
         case MOE_CALL_EXPERT_FFN: ok(); return ffn_ws(shape);
+        case MOE_CALL_ROUTE: ok(); return route_ws(shape);
         case MOE_CALL_FORWARD: {
-            size_t off[MOE_FWD_NUM_SLOTS + 3];
+            size_t off[kFwdTotal + 1];
             forward_layout(shape, off);
             ok();
-            return off[MOE_FWD_NUM_SLOTS + 2];
+            return off[kFwdTotal];
         }
         default: fail(MOE_ERR_INVALID_ARG, "unknown call %d", call); return 0;
     }
@@ -153,14 +163,14 @@ int moe_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset) {
     if (st != MOE_OK) return st;
     if (slot < 0 || slot >= MOE_FWD_NUM_SLOTS) return fail(MOE_ERR_INVALID_ARG, "unknown slot %d", slot);
     if (offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "offset is NULL");
-    size_t off[MOE_FWD_NUM_SLOTS + 3];
+    size_t off[kFwdTotal + 1];
     forward_layout(shape, off);
     *offset = off[slot];
     return ok();
 }
 
 int moe_route(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
-              float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+              float* logits, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -171,8 +181,11 @@ int moe_route(const moe_shape_t* shape, const uint16_t* x, const float* w_router
     MOE_CHECK_PTR(logits);
     MOE_CHECK_PTR(topk_idx);
     MOE_CHECK_PTR(topk_w);
+    st = check_ws(ws, ws_bytes, route_ws(shape));
+    if (st != MOE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, shape->T, shape->d, shape->E, s);
+    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, shape->T, shape->d, shape->E,
+                                             static_cast<uint16_t*>(ws), s);
     if (err != hipSuccess) return hip_status(err, "router_gemm launch");
     err = moe::launch_topk_softmax(logits, shape->T, shape->E, shape->k, topk_idx, topk_w, s);
     return hip_status(err, "topk_softmax launch");
@@ -315,9 +328,9 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     MOE_CHECK_PTR(w_up);
     MOE_CHECK_PTR(w_down);
     MOE_CHECK_PTR(out);
-    size_t off[MOE_FWD_NUM_SLOTS + 3];
+    size_t off[kFwdTotal + 1];
     forward_layout(shape, off);
-    st = check_ws(ws, ws_bytes, off[MOE_FWD_NUM_SLOTS + 2]);
+    st = check_ws(ws, ws_bytes, off[kFwdTotal]);
     if (st != MOE_OK) return st;
     char* base = static_cast<char*>(ws);
     auto at = [&](int slot) { return static_cast<void*>(base + off[slot]); };
@@ -329,13 +342,14 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     int32_t* row_src = static_cast<int32_t*>(at(MOE_FWD_ROW_SRC));
     uint16_t* h_act = static_cast<uint16_t*>(at(MOE_FWD_H));
     float* y_rows = static_cast<float*>(at(MOE_FWD_Y));
-    int32_t* count_ws = static_cast<int32_t*>(at(MOE_FWD_NUM_SLOTS));
-    const FfnWs fw = ffn_carve(shape, at(MOE_FWD_NUM_SLOTS + 1));
+    int32_t* count_ws = static_cast<int32_t*>(at(kFwdPermuteWs));
+    const FfnWs fw = ffn_carve(shape, at(kFwdFfnWs));
+    uint16_t* router_parts = static_cast<uint16_t*>(at(kFwdRouteWs));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t T = shape->T, n = shape->T * shape->k;
     const int d = shape->d, E = shape->E, k = shape->k, h = shape->h;
 
-    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, T, d, E, s);
+    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, T, d, E, router_parts, s);
     if (err != hipSuccess) return hip_status(err, "router_gemm launch");
     err = moe::launch_topk_softmax(logits, T, E, k, idx, w, s);
     if (err != hipSuccess) return hip_status(err, "topk_softmax launch");

@@ -6,6 +6,8 @@
 #include "device_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace moe {
 
 // ---------------------------------------------------------------- gate GEMM
@@ -13,78 +15,76 @@ namespace moe {
 // logits[t, e] = sum_i x[t, i] * w[e, i] (+ bias[e]), x bf16, w float32.
 //
 // Every float32 weight is split exactly into three bfloat16 terms,
-// w = hi + mid + lo (8 + 8 + 8 significant bits; the RNE residues are exactly
-// representable), and each product x * part is exact in float32 because both
-// factors carry at most 8 significant bits. The three products accumulate in
-// the MFMA's float32 accumulator, so the result is a float32 accumulation of
-// exact products, on bf16 matrix cores (16x the float32 vector rate).
+// w = hi + mid + lo (8 + 8 + 8 significant bits; each term is the RNE rounding
+// of what the previous ones left, and that residue is exact), once per call by
+// router_split_kernel. Each product x * part is exact in float32 because both
+// factors carry at most 8 significant bits, and the three products accumulate
+// in the MFMA's float32 accumulator: a float32 accumulation of exact products
+// on the bf16 matrix cores.
 //
-// Tile: 64 tokens x 64 experts per 256-thread workgroup, K step 64;
-// wave (wm, wn) owns a 32 x 32 quarter as 2 x 2 blocks of 16 x 16.
+// Tile: 64 tokens x 64 experts per 256-thread workgroup, K step 64, the token
+// rows and the three weight parts staged in LDS (double-buffered); wave
+// (wm, wn) owns a 32 x 32 quarter as 2 x 2 blocks of 16 x 16.
 
 constexpr int kRBM = 64, kRBN = 64, kRBK = 64;
-constexpr int kRStride = kRBK + 8;  // bf16 per LDS row: 144 B keeps 16-B reads conflict-free
+constexpr int kRStride = kRBK + 16;  // bf16 per LDS row (32 B of padding: conflict-free 16-B reads)
+
+// w [E, d] float32 -> parts [3][E][d] bf16 with w = parts[0] + parts[1] + parts[2] exactly.
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w, int64_t n,
+                                                           uint16_t* __restrict__ parts) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const float v = w[i];
+        const uint16_t h = f32_to_bf16_bits(v);
+        const float r1 = v - bf16_bits_to_f32(h);
+        const uint16_t m = f32_to_bf16_bits(r1);
+        const float r2 = r1 - bf16_bits_to_f32(m);
+        parts[i] = h;
+        parts[n + i] = m;
+        parts[2 * n + i] = f32_to_bf16_bits(r2);
+    }
+}
 
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
-                                                          const float* __restrict__ w,
+                                                          const uint16_t* __restrict__ parts,
                                                           const float* __restrict__ bias,
-                                                          float* __restrict__ logits, int64_t T,
-                                                          int d, int E) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[kRBM * kRStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[3][kRBN * kRStride];
+                                                          float* __restrict__ logits, int64_t T, int d, int E) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kRBM * kRStride];
+    __shared__ __attribute__((aligned(16))) uint16_t sB[2][3][kRBN * kRStride];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int n0 = blockIdx.x * kRBN;
     const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRBM;
+    const int64_t pn = static_cast<int64_t>(E) * d;  // elements per weight part
 
-    // global -> register staging: thread owns one row and a 16-wide k chunk
-    const int ld_row = tid >> 2, ld_part = tid & 3;
-    const bool a_ok = (m0 + ld_row) < T;
-    const bool b_ok = (n0 + ld_row) < E;
-    const uint16_t* a_src = x + (m0 + ld_row) * static_cast<int64_t>(d) + ld_part * 16;
-    const float* b_src = w + static_cast<int64_t>(n0 + ld_row) * d + ld_part * 16;
-
-    uint4 a_reg[2];
-    float4 b_reg[4];
+    // global -> register staging: 512 16-byte chunks per 64 x 64 tile, two per
+    // thread (rows tid / 8 and tid / 8 + 32, chunk tid % 8); rows past the
+    // matrix end re-read its last row (results never stored)
+    const int ld_row = tid >> 3, ld_col = 8 * (tid & 7);
+    int64_t a_off[2], b_off[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        a_off[p] = min(m0 + ld_row + 32 * p, T - 1) * d + ld_col;
+        b_off[p] = static_cast<int64_t>(min(n0 + ld_row + 32 * p, E - 1)) * d + ld_col;
+    }
+    u32x4 a_reg[2], b_reg[3][2];
     auto load_tile = [&](int k0) {
-        if (a_ok) {
-            a_reg[0] = *reinterpret_cast<const uint4*>(a_src + k0);
-            a_reg[1] = *reinterpret_cast<const uint4*>(a_src + k0 + 8);
-        } else {
-            a_reg[0] = a_reg[1] = make_uint4(0, 0, 0, 0);
-        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            b_reg[q] = b_ok ? *reinterpret_cast<const float4*>(b_src + k0 + 4 * q)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p = 0; p < 2; ++p) {
+            a_reg[p] = *reinterpret_cast<const u32x4*>(x + a_off[p] + k0);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) b_reg[q][p] = *reinterpret_cast<const u32x4*>(parts + q * pn + b_off[p] + k0);
+        }
     };
-    auto store_tile = [&]() {
-        uint16_t* a_dst = sA + ld_row * kRStride + ld_part * 16;
-        reinterpret_cast<uint4*>(a_dst)[0] = a_reg[0];
-        reinterpret_cast<uint4*>(a_dst)[1] = a_reg[1];
-        uint16_t hi[16], mid[16], lo[16];
+    auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float v[4] = {b_reg[q].x, b_reg[q].y, b_reg[q].z, b_reg[q].w};
+        for (int p = 0; p < 2; ++p) {
+            const int off = (ld_row + 32 * p) * kRStride + ld_col;
+            *reinterpret_cast<u32x4*>(&sA[buf][off]) = a_reg[p];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint16_t h = f32_to_bf16_bits(v[c]);
-                const float r1 = v[c] - bf16_bits_to_f32(h);
-                const uint16_t m = f32_to_bf16_bits(r1);
-                const float r2 = r1 - bf16_bits_to_f32(m);
-                hi[4 * q + c] = h;
-                mid[4 * q + c] = m;
-                lo[4 * q + c] = f32_to_bf16_bits(r2);
-            }
-        }
-        const int off = ld_row * kRStride + ld_part * 16;
-        uint16_t* parts[3] = {hi, mid, lo};
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-            reinterpret_cast<uint4*>(sB[p] + off)[0] = reinterpret_cast<const uint4*>(parts[p])[0];
-            reinterpret_cast<uint4*>(sB[p] + off)[1] = reinterpret_cast<const uint4*>(parts[p])[1];
+            for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4*>(&sB[buf][q][off]) = b_reg[q][p];
         }
     };
 
@@ -95,31 +95,35 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
+    const int nk = d / kRBK;
     load_tile(0);
-    for (int k0 = 0; k0 < d; k0 += kRBK) {
-        store_tile();
-        __syncthreads();
-        if (k0 + kRBK < d) load_tile(k0 + kRBK);
+    store_tile(0);
+    __syncthreads();
+    for (int step = 0; step < nk; ++step) {
+        const int cur = step & 1;
+        if (step + 1 < nk) load_tile((step + 1) * kRBK);
 #pragma unroll
         for (int s = 0; s < kRBK / 32; ++s) {
             bf16x8 a[2], b[3][2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 32 + i * 16 + frag_row) * kRStride + s * 32 + frag_k);
+                a[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][(wm * 32 + i * 16 + frag_row) * kRStride + s * 32 + frag_k]);
 #pragma unroll
-            for (int p = 0; p < 3; ++p)
+            for (int q = 0; q < 3; ++q)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    b[p][j] = *reinterpret_cast<const bf16x8*>(sB[p] + (wn * 32 + j * 16 + frag_row) * kRStride + s * 32 + frag_k);
+                    b[q][j] = *reinterpret_cast<const bf16x8*>(
+                        &sB[cur][q][(wn * 32 + j * 16 + frag_row) * kRStride + s * 32 + frag_k]);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    acc[i][j] = mfma_16x16x32(a[i], b[2][j], acc[i][j]);
+                    acc[i][j] = mfma_16x16x32(a[i], b[2][j], acc[i][j]);  // smallest part first
                     acc[i][j] = mfma_16x16x32(a[i], b[1][j], acc[i][j]);
                     acc[i][j] = mfma_16x16x32(a[i], b[0][j], acc[i][j]);
                 }
         }
+        if (step + 1 < nk) store_tile(cur ^ 1);
         __syncthreads();
     }
 
@@ -206,10 +210,15 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 
 // ------------------------------------------------------------------ launchers
 
-hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
-                              int64_t T, int d, int E, hipStream_t stream) {
+size_t router_parts_bytes(int d, int E) { return sizeof(uint16_t) * 3 * static_cast<size_t>(E) * d; }
+
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits, int64_t T, int d,
+                              int E, uint16_t* parts, hipStream_t stream) {
+    const int64_t n = static_cast<int64_t>(E) * d;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, w, n, parts);
     dim3 grid((E + kRBN - 1) / kRBN, static_cast<unsigned>((T + kRBM - 1) / kRBM));
-    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, w, bias, logits, T, d, E);
+    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, parts, bias, logits, T, d, E);
     return hipGetLastError();
 }
 

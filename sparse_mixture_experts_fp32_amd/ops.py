@@ -69,9 +69,10 @@ def moe_route(x, w_router, router_bias, k: int, *, out=None):
     _need(logits, "logits", "f32", (T, E), dev)
     _need(idx, "topk_idx", "i32", (T, k), dev)
     _need(w, "topk_w", "f32", (T, k), dev)
+    ws = workspace(s, _lib.MOE_CALL_ROUTE, dev)
     with torch.cuda.device(dev):
         _lib.check(_lib.lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                                      _ptr(logits), _ptr(idx), _ptr(w), _stream(dev)))
+                                      _ptr(logits), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(), _stream(dev)))
     return logits, idx, w
 
 

@@ -50,7 +50,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 2
+    assert L.moe_abi_version() == lib.ABI_VERSION == 3
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -74,7 +74,7 @@ def _shape(lib, **kw):
 def test_bad_shapes_rejected(lib, bad, status):
     s = _shape(lib, **bad)
     fake = ctypes.c_void_p(4096)
-    st = lib.lib.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, fake, None)
+    st = lib.lib.moe_route(ctypes.byref(s), fake, fake, None, fake, fake, fake, fake, 1 << 30, None)
     assert st == status, lib.lib.moe_last_error()
     assert lib.lib.moe_last_error()
     assert lib.lib.moe_workspace_bytes(ctypes.byref(s), 2) == 0
@@ -85,11 +85,11 @@ def test_null_and_misaligned_pointers_rejected(lib):
     a = ctypes.c_void_p(4096)
     mis = ctypes.c_void_p(4096 + 2)
     L = lib.lib
-    assert L.moe_route(ctypes.byref(s), None, a, None, a, a, a, None) == 1
+    assert L.moe_route(ctypes.byref(s), None, a, None, a, a, a, a, 1 << 30, None) == 1
     assert b"x is NULL" in L.moe_last_error()
-    assert L.moe_route(ctypes.byref(s), mis, a, None, a, a, a, None) == 1
+    assert L.moe_route(ctypes.byref(s), mis, a, None, a, a, a, a, 1 << 30, None) == 1
     assert b"aligned" in L.moe_last_error()
-    assert L.moe_route(ctypes.byref(s), a, a, mis, a, a, a, None) == 1
+    assert L.moe_route(ctypes.byref(s), a, a, mis, a, a, a, a, 1 << 30, None) == 1
     assert L.moe_topk_softmax(ctypes.byref(s), None, a, a, None) == 1
     assert L.moe_combine(ctypes.byref(s), a, a, None, a, None) == 1
     assert L.moe_expert_ffn(ctypes.byref(s), a, None, a, a, a, None, a, a, a, 1 << 20, None) == 1
@@ -100,7 +100,7 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, mis, a, 1 << 20, None) == 1
     assert L.moe_permute(ctypes.byref(s), None, a, a, a, a, a, a, 1 << 20, None) == 1
     assert L.moe_forward(ctypes.byref(s), a, a, None, a, a, a, None, a, 1 << 30, None) == 1
-    assert L.moe_route(None, a, a, None, a, a, a, None) == 1
+    assert L.moe_route(None, a, a, None, a, a, a, a, 1 << 30, None) == 1
 
 
 def test_workspace_checks(lib):
@@ -110,6 +110,10 @@ def test_workspace_checks(lib):
     need_p = lib.workspace_bytes(s, lib.MOE_CALL_PERMUTE)
     need_f = lib.workspace_bytes(s, lib.MOE_CALL_EXPERT_FFN)
     need_fw = lib.workspace_bytes(s, lib.MOE_CALL_FORWARD)
+    need_r = lib.workspace_bytes(s, lib.MOE_CALL_ROUTE)
+    assert need_r >= 3 * 2 * GOOD["E"] * GOOD["d"] and need_r % 256 == 0
+    assert L.moe_route(ctypes.byref(s), a, a, None, a, a, a, None, need_r, None) == 3
+    assert L.moe_route(ctypes.byref(s), a, a, None, a, a, a, a, need_r - 1, None) == 3
     assert need_p > 0 and need_f > 0 and need_fw > 0
     assert need_p % 256 == 0 and need_f % 256 == 0 and need_fw % 256 == 0
     assert L.moe_permute(ctypes.byref(s), a, a, a, a, a, a, None, need_p, None) == 3
@@ -143,7 +147,7 @@ def test_forward_workspace_layout(lib):
 def test_zero_tokens_is_a_noop(lib):
     s = _shape(lib, T=0)
     L = lib.lib
-    assert L.moe_route(ctypes.byref(s), None, None, None, None, None, None, None) == 0
+    assert L.moe_route(ctypes.byref(s), None, None, None, None, None, None, None, 0, None) == 0
     assert L.moe_combine(ctypes.byref(s), None, None, None, None, None) == 0
     assert L.moe_forward(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None) == 0
     assert L.moe_expert_ffn(ctypes.byref(s), None, None, None, None, None, None, None, None, None, 0, None) == 0
