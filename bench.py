@@ -29,6 +29,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), d=7168 E=256 top-4"
+# HBM bytes per launch of the dominant kernel, from two rocprofv3 counter runs
+# (FETCH_SIZE, WRITE_SIZE scaled by a copy kernel of known size), recorded with
+# a hash of the kernel's sources: reported only while those sources are unchanged.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
@@ -157,6 +161,24 @@ def cpu_baseline(inp, cfg, n_experts):
     }
 
 
+def measured_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter record, or None if the kernel changed since."""
+    import hashlib
+    path = TRAFFIC_RECORD.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        p = os.path.join(ROOT, src)
+        if not os.path.exists(p):
+            return None
+        with open(p, "rb") as g:
+            h.update(g.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -176,7 +198,11 @@ def main():
         sys.exit(1)
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
-    inp = make_inputs(cfg, device=dev)
+    def progress(n):
+        print(f"[bench] {cfg.name}: drew {n} of {cfg.E} experts' weights", file=sys.stderr, flush=True)
+
+    inp = make_inputs(cfg, device=dev, progress=progress)
+    print(f"[bench] {cfg.name}: inputs ready", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     layer = Layer(lib, inp, cfg, dev)
 
@@ -252,7 +278,7 @@ def main():
                          "down_gbs": down_gbs, "down_hbm_frac": down_gbs / HBM_PEAK_GBS},
         "roofline": {"kernel": "grouped_ffn_kernel<gated> (gate/up pass + SwiGLU)", "bound": "hbm",
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes": gu_bytes},
+                     "traffic": measured_traffic(cfg.name), "algorithmic_bytes": gu_bytes},
     }
     if args.cpu_experts > 0:
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_experts)

@@ -227,9 +227,11 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
     } else {
         // Weights three K steps ahead (a ring of four register sets), A rows two
         // steps ahead (two register sets) and written to LDS one step ahead (two
-        // buffers). Step i: load weights i+3 and A rows i+2, multiply step i,
-        // store A rows i+1, barrier. Four steps per loop trip, so every ring
-        // index is a compile-time constant.
+        // buffers). Step i: load A rows i+2, then weights i+3, multiply step i,
+        // store A rows i+1, barrier. Vector-memory counters retire in issue
+        // order, so the A rows are issued first: waiting for A rows i+1 at the
+        // end of step i then does not wait for weights i+2. Four steps per loop
+        // trip, so every ring index is a compile-time constant.
         u32x4 ar[2][kAPasses];
         bf16x8 bw[4][kNB][kSub];
         load_rows(ar[0], a_src, a_off, 0);
@@ -242,8 +244,8 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
 #define MOE_DEEP_STEP(U)                                                                                  \
     {                                                                                                     \
         const int step = s0 + (U);                                                                        \
-        load_weights(bw[((U) + 3) % 4], wb, min(step + 3, nk - 1) * kKS);                                 \
         load_rows(ar[(U) % 2], a_src, a_off, min(step + 2, nk - 1) * kKS);                                \
+        load_weights(bw[((U) + 3) % 4], wb, min(step + 3, nk - 1) * kKS);                                 \
         if (wave_on && step < nk)                                                                         \
             mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[(U) % 2], bw[(U) % 4]);            \
         store_rows<kAPasses, kPassStride>(a_dst[((U) + 1) % 2], ar[((U) + 1) % 2]);                       \
@@ -377,9 +379,10 @@ hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows,
 
 // 8 waves x 32 weight rows, K step 64, m-tiles of up to 192 rows, LDS rows padded
 // by 32 B (chosen by measurement on the prefill, decode, many-expert and skewed
-// loads: padding by 16 B showed bank conflicts on gfx950, deeper prefetch and
-// 2-D wave grids were slower).
-using GateUpCfg = GemmCfg<1, 8, 2, 64, 12, false, 16>;
+// loads: padding by 16 B showed bank conflicts on gfx950, 2-D wave grids and
+// 4-wave workgroups were slower). The gate/up pass (K = d) keeps weights three
+// steps ahead; the down pass (K = h, a quarter as deep) measured best one ahead.
+using GateUpCfg = GemmCfg<1, 8, 2, 64, 12, true, 16>;
 using DownCfg = GemmCfg<1, 8, 2, 64, 12, false, 16>;
 static_assert(GateUpCfg::kBM == DownCfg::kBM, "both passes share one m-tile list");
 

@@ -121,7 +121,7 @@ def router_bias_for(cfg: MoEConfig, device: str = "cpu") -> Optional[torch.Tenso
 
 
 def make_inputs(cfg: MoEConfig, device: str = "cpu", gen_device: Optional[str] = None,
-                experts: bool = True) -> MoEInputs:
+                experts: bool = True, progress=None) -> MoEInputs:
     """Draw every input of one layer invocation.
 
     gen_device is where the random numbers are drawn ("cpu" or "cuda"); the
@@ -129,7 +129,8 @@ def make_inputs(cfg: MoEConfig, device: str = "cpu", gen_device: Optional[str] =
     must draw a workload once and hand the same tensors to both sides. By
     default small workloads are drawn on the CPU (reproducible everywhere)
     and large ones on the target device (drawing tens of GB of normals on the
-    host would take minutes).
+    host would take minutes). `progress`, if given, is called with the number
+    of experts drawn so far, every 64 experts.
     """
     if gen_device is None:
         gen_device = "cpu" if cfg.expert_weight_bytes() <= (256 << 20) else str(device)
@@ -149,6 +150,8 @@ def make_inputs(cfg: MoEConfig, device: str = "cpu", gen_device: Optional[str] =
             w_gate[e].copy_(_normal((h, d), 1.0 / math.sqrt(d), _gen(gen_device, cfg.seed, TAG_GATE, e), gen_device).to(torch.bfloat16))
             w_up[e].copy_(_normal((h, d), 1.0 / math.sqrt(d), _gen(gen_device, cfg.seed, TAG_UP, e), gen_device).to(torch.bfloat16))
             w_down[e].copy_(_normal((d, h), 1.0 / math.sqrt(h), _gen(gen_device, cfg.seed, TAG_DOWN, e), gen_device).to(torch.bfloat16))
+            if progress is not None and (e + 1) % 64 == 0:
+                progress(e + 1)
     else:
         w_gate = w_up = w_down = None
     return MoEInputs(cfg, x, w_router, bias, w_gate, w_up, w_down)
