@@ -205,6 +205,8 @@ def main():
     print(f"[bench] {cfg.name}: inputs ready", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     layer = Layer(lib, inp, cfg, dev)
+    note = lambda msg: print(f"[bench] {cfg.name}: {msg}", file=sys.stderr, flush=True)  # noqa: E731
+    note("buffers allocated")
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -214,10 +216,12 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
+        note("copy probe done")
 
     for _ in range(args.warmup):
         layer.step()
     torch.cuda.synchronize()
+    note(f"{args.warmup} warmup steps done")
 
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
@@ -230,6 +234,7 @@ def main():
     stop.record(layer.stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / K
+    note(f"{K} timed steps done")
     gpu_ms = start.elapsed_time(stop) / K
     gate_up_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     down_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
@@ -240,6 +245,7 @@ def main():
     torch.cuda.synchronize()
     assert torch.equal(ref_out, layer.out), "bench step and moe_forward disagree"
     del fwd, ref_out
+    note("bench step equals moe_forward bit for bit")
 
     T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
     n = T * k
@@ -281,6 +287,7 @@ def main():
                      "traffic": measured_traffic(cfg.name), "algorithmic_bytes": gu_bytes},
     }
     if args.cpu_experts > 0:
+        note("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_experts)
     print(json.dumps(result), flush=True)
 
