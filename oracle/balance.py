@@ -40,7 +40,7 @@ Readings where the pages are silent or garbled (also listed in the design notes)
     bin = floor(fl(fl(margin - lo) / width)), clamped to [0, B - 1]; so
     margins below lo count in bin 0 and those at or above lo + B*width in
     bin B - 1. The bin range (lo, width) is lost on the page and is a
-    parameter.
+    parameter: two float32 values, used as such in the quantile as well.
   * the quantile is read from the histogram with the grouped-data formula:
     the first bin b whose cumulative count C_b reaches p*m (m = the row's
     total, p = 1 - k/E), then Q = lo + width * (b + (p*m - C_{b-1}) / H_b),
@@ -170,7 +170,9 @@ def qb_histogram(logits, alpha, lo: float, width: float, n_bins: int) -> np.ndar
 def qb_quantile(hist, k: int, lo: float, width: float) -> np.ndarray:
     """[AQ] (1 - k/E)-quantile of each histogram row by the grouped-data formula
     (float64 [E]; NaN for an empty row). The bin is chosen in exact integer
-    arithmetic: the first b with C_b * E >= m * (E - k)."""
+    arithmetic: the first b with C_b * E >= m * (E - k). lo and width are the
+    float32 values that define the bins (as in qb_bin)."""
+    lo, width = float(np.float32(lo)), float(np.float32(width))
     H = _i64(hist)
     E, B = H.shape
     Q = np.full(E, np.nan)
