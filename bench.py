@@ -13,7 +13,10 @@ HIP events on that stream time each GEMM pass inside every timed step.
 
 Prints one JSON line: whole-layer tokens/s, the grouped GEMM's TFLOP/s and
 MFMA fraction, the roofline of the dominant kernel (the gate/up pass) and the
-CPU oracle's rate on a bounded sample of the same workload.
+CPU oracle's rate on a bounded sample of the same workload. The "balance"
+object times the router's load-balancing calls on the step's own logits: one
+Quantile Balancing step (moe_qb_route, moe_qb_histogram with 1000 bins,
+moe_qb_update) and moe_aux_loss, each against HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -98,6 +101,75 @@ class Layer:
         if ev is not None:
             ev[2].record(self.stream)
         c(L.moe_combine(sh, P(self.y_rows), P(self.row_of), P(self.w), P(self.out), sp))
+
+
+class Balance:
+    """Buffers and C-ABI calls of the load-balancing step on a layer's logits."""
+
+    BINS, LO, WIDTH = 1000, -16.0, 0.03125
+
+    def __init__(self, layer):
+        import torch
+        lib, cfg, dev = layer.lib, layer.cfg, layer.dev
+        self.layer, self.lib = layer, lib
+        T, E, k = cfg.T, cfg.E, cfg.k
+        e = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        self.bias = torch.zeros(E, dtype=torch.float32, device=dev)
+        self.idx = e(T, k, dt=torch.int32)
+        self.w = e(T, k, dt=torch.float32)
+        self.alpha = e(T, dt=torch.float32)
+        self.hist = e(E, self.BINS, dt=torch.int32)
+        self.prob_mean = e(E, dt=torch.float32)
+        self.aux = e(1, dt=torch.float32)
+        self.ws_aux = e(max(1, lib.workspace_bytes(layer.shape, lib.MOE_CALL_AUX_LOSS)), dt=torch.uint8)
+        self.ok = k < E and k <= 63  # Quantile Balancing selects k + 1 experts
+
+    def step(self, ev=None):
+        """QB route, histogram, update (bias updated in place), then the aux loss."""
+        L, P, sh, sp, c = self.lib.lib, self.layer.P, self.layer.sh, self.layer.sp, self.lib.check
+        st = self.layer.stream
+        rec = (lambda i: ev[i].record(st)) if ev is not None else (lambda i: None)
+        f = ctypes.c_float
+        rec(0)
+        if self.ok:
+            c(L.moe_qb_route(sh, P(self.layer.logits), P(self.bias), P(self.idx), P(self.w), P(self.alpha), sp))
+            rec(1)
+            c(L.moe_qb_histogram(sh, P(self.layer.logits), P(self.alpha), f(self.LO), f(self.WIDTH), self.BINS,
+                                 P(self.hist), sp))
+            rec(2)
+            c(L.moe_qb_update(sh, P(self.hist), f(self.LO), f(self.WIDTH), self.BINS, P(self.bias), P(self.bias), sp))
+        else:
+            rec(1)
+            rec(2)
+        rec(3)
+        c(L.moe_aux_loss(sh, P(self.layer.logits), P(self.prob_mean), P(self.aux), P(self.ws_aux),
+                         self.ws_aux.numel(), sp))
+        rec(4)
+
+    def measure(self, reps):
+        """Mean time of each call over `reps` steps (HIP events on the layer's stream) and its rate."""
+        import torch
+        cfg = self.layer.cfg
+        T, E, k, B = cfg.T, cfg.E, cfg.k, self.BINS
+        for _ in range(3):
+            self.step()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(reps)]
+        for r in range(reps):
+            self.step(evs[r])
+        torch.cuda.synchronize()
+        us = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / reps * 1e3 for i in range(4)]
+        # algorithmic bytes: each input read once, each output written once
+        nbytes = {"qb_route": 4.0 * T * E + 4.0 * E + 8.0 * T * k + 4.0 * T,
+                  "qb_histogram": 4.0 * T * E + 4.0 * T + 4.0 * E * B,
+                  "qb_update": 4.0 * E * B + 8.0 * E,
+                  "aux_loss": 4.0 * T * E + 4.0 * E + 4.0}
+        out = {"bins": B, "reps": reps}
+        for name, t in zip(["qb_route", "qb_histogram", "qb_update", "aux_loss"], us):
+            if not self.ok and name.startswith("qb_"):
+                continue
+            gbs = nbytes[name] / (t * 1e-6) / 1e9
+            out[name] = {"us": t, "bytes": nbytes[name], "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+        return out
 
 
 def cpu_baseline(inp, cfg, n_experts):
@@ -286,6 +358,8 @@ def main():
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(cfg.name), "algorithmic_bytes": gu_bytes},
     }
+    result["balance"] = Balance(layer).measure(max(K, 10))
+    note("load-balancing calls timed")
     if args.cpu_experts > 0:
         note("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_experts)

@@ -13,7 +13,9 @@
  *  - same page, section "Systems Optimization, Load Balancing, and
  *    Post-Training Alignment": per-expert token counts vary from step to step,
  *    and waiting on them on the host stalls the device; nothing here reads
- *    counts back to the host.
+ *    counts back to the host. The same section gives Quantile Balancing, the
+ *    router-bias update of moe_qb_route / moe_qb_histogram / moe_qb_update;
+ *    moe_aux_loss is the first page's auxiliary balance loss.
  *
  * Conventions shared by every call
  *  - All tensors are dense, row-major (C order), on the device, 16-byte
@@ -44,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -67,7 +69,8 @@ typedef enum moe_call {
     MOE_CALL_PERMUTE = 0,
     MOE_CALL_EXPERT_FFN = 1,
     MOE_CALL_FORWARD = 2,
-    MOE_CALL_ROUTE = 3
+    MOE_CALL_ROUTE = 3,
+    MOE_CALL_AUX_LOSS = 4
 } moe_call_t;
 
 /* Intermediates that moe_forward keeps in its workspace (see moe_forward_ws_offset). */
@@ -224,6 +227,69 @@ int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* ro
 int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
                 const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
                 const uint16_t* w_down, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_aux_loss -- the auxiliary load-balancing loss that the gating forward
+ * pass returns ("Kimi K3: The Open Model That Just Cornered the AI Frontier",
+ * section "Mixture-of-Experts with Dynamic Load Balancing"): each expert's
+ * softmax probability averaged over the T tokens, and the sum over experts of
+ * its squared distance from the uniform share 1/E. The loss weight belongs to
+ * the training objective and is not applied.
+ *
+ *  logits    [T, E] float32 (read)
+ *  prob_mean [E]    float32 out: mean_t softmax(logits[t])[e] (summed in float64)
+ *  aux_loss  [1]    float32 out: sum_e (prob_mean[e] - 1/E)^2 (evaluated in float64)
+ *  ws, ws_bytes  workspace of at least moe_workspace_bytes(shape, MOE_CALL_AUX_LOSS)
+ * T == 0 is a no-op (outputs untouched: an empty batch has no mean). d and h
+ * of the shape are checked but not used.
+ */
+int moe_aux_loss(const moe_shape_t* shape, const float* logits, float* prob_mean, float* aux_loss,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Quantile Balancing ("Kimi K3: Open Frontier Intelligence", section "Systems
+ * Optimization, Load Balancing, and Post-Training Alignment"): balancing as
+ * the dual of the token-to-expert assignment problem. One step is three calls:
+ *   moe_qb_route      top-(k+1) routing on the biased scores: the k chosen
+ *                     experts and each token's cutoff alpha;
+ *   moe_qb_histogram  per-expert histogram of the margins logits - alpha
+ *                     (ranks that share the batch would add their histograms
+ *                     here, one integer all-reduce);
+ *   moe_qb_update     each expert's new bias, minus the (1 - k/E)-quantile of
+ *                     its margins read off the histogram.
+ * The score is the router logit; the bias moves the selection only. These
+ * calls need k < E and k <= 63 (the cutoff is the (k+1)-th score); d and h
+ * of the shape are checked but not used.
+ *
+ * moe_qb_route:
+ *  logits   [T, E] float32 (read); qb_bias [E] float32 (read)
+ *  topk_idx [T, k] int32 out: the k largest fl32(logits[t, e] + qb_bias[e]),
+ *           largest first, ties to the lower id
+ *  topk_w   [T, k] float32 out: softmax of the unbiased logits renormalised
+ *           over the chosen k
+ *  alpha    [T]    float32 out: the (k+1)-th largest biased score
+ *
+ * moe_qb_histogram: hist[e, b] = number of tokens whose margin
+ *  fl32(logits[t, e] - alpha[t]) falls in bin b = floor(fl32(fl32(margin - lo) / width)),
+ *  clamped to [0, n_bins - 1]: bin b covers [lo + b width, lo + (b+1) width)
+ *  and margins outside the range count in the end bins.
+ *  logits [T, E], alpha [T] float32 (read); hist [E, n_bins] int32 (overwritten).
+ *  lo finite, width finite and > 0, 1 <= n_bins <= 4096. T == 0 gives zeros.
+ *
+ * moe_qb_update: for each expert e with m = sum_b hist[e, b] > 0, b is the
+ *  first bin whose cumulative count C_b has C_b * E >= m * (E - k) (exact
+ *  integers) and Q = lo + width * (b + (m (E - k) / E - C_{b-1}) / hist[e, b])
+ *  in float64; bias_out[e] = -Q rounded to float32. A row with m == 0 copies
+ *  bias_in[e].
+ *  hist [E, n_bins] int32 (read; counts >= 0); bias_in [E] float32 (read);
+ *  bias_out [E] float32 (written; may be bias_in itself). shape->T is not used.
+ */
+int moe_qb_route(const moe_shape_t* shape, const float* logits, const float* qb_bias,
+                 int32_t* topk_idx, float* topk_w, float* alpha, void* stream);
+int moe_qb_histogram(const moe_shape_t* shape, const float* logits, const float* alpha, float lo,
+                     float width, int32_t n_bins, int32_t* hist, void* stream);
+int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float width,
+                  int32_t n_bins, const float* bias_in, float* bias_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,9 +22,10 @@ MOE_CALL_PERMUTE = 0
 MOE_CALL_EXPERT_FFN = 1
 MOE_CALL_FORWARD = 2
 MOE_CALL_ROUTE = 3
+MOE_CALL_AUX_LOSS = 4
 
 FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class MoeShape(ctypes.Structure):
@@ -58,6 +59,10 @@ def _load():
         "moe_expert_down": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [S, P, P, P, P, P]),
         "moe_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_aux_loss": (ctypes.c_int, [S, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_qb_route": (ctypes.c_int, [S, P, P, P, P, P, P]),
+        "moe_qb_histogram": (ctypes.c_int, [S, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32, P, P]),
+        "moe_qb_update": (ctypes.c_int, [S, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

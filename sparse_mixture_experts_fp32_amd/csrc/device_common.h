@@ -45,4 +45,24 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
     return v;
 }
 
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Monotone map of a float to uint32 for selection keys: larger float, larger key;
+// -0.0 and +0.0 map to one key; NaN maps to 0, below every number.
+__device__ __forceinline__ uint32_t order_key(float v) {
+    if (v != v) return 0u;     // NaN: below every number
+    if (v == 0.0f) v = 0.0f;   // -0.0 ties +0.0
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+    if (k == 0u) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 }  // namespace moe

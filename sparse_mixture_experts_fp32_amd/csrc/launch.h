@@ -33,4 +33,15 @@ hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T,
                           int d, int k, int64_t n_rows, float* out, hipStream_t stream);
 
+hipError_t launch_qb_select(const float* logits, const float* bias, int64_t T, int E, int k, int32_t* topk_idx,
+                            float* topk_w, float* alpha, hipStream_t stream);
+int qb_max_bins();
+hipError_t launch_qb_histogram(const float* logits, const float* alpha, int64_t T, int E, float lo, float width,
+                               int n_bins, int32_t* hist, hipStream_t stream);
+hipError_t launch_qb_update(const int32_t* hist, int E, int k, int n_bins, float lo, float width,
+                            const float* bias_in, float* bias_out, hipStream_t stream);
+size_t aux_ws_bytes(int64_t T, int E);
+hipError_t launch_aux_loss(const float* logits, int64_t T, int E, float* prob_mean, float* aux_loss, void* ws,
+                           hipStream_t stream);
+
 }  // namespace moe

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -94,6 +95,28 @@ size_t ffn_ws(const moe_shape_t* s) {
     return ffn_tiles_bytes(s) + align_up(sizeof(int32_t) * (static_cast<size_t>(s->E) + 1));
 }
 
+size_t aux_ws(const moe_shape_t* s) {
+    if (s->T == 0) return 0;
+    return align_up(moe::aux_ws_bytes(s->T, s->E));
+}
+
+// Quantile Balancing selects k + 1 experts per token with one wavefront.
+int check_qb_shape(const moe_shape_t* s) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    if (s->k >= s->E || s->k > 63)
+        return fail(MOE_ERR_INVALID_ARG, "Quantile Balancing needs k < E and k <= 63 (k = %d, E = %d)", s->k, s->E);
+    return MOE_OK;
+}
+
+int check_bins(float lo, float width, int32_t n_bins) {
+    if (!std::isfinite(lo)) return fail(MOE_ERR_INVALID_ARG, "lo is not finite");
+    if (!std::isfinite(width) || !(width > 0.f)) return fail(MOE_ERR_INVALID_ARG, "width must be finite and > 0");
+    if (n_bins < 1 || n_bins > moe::qb_max_bins())
+        return fail(MOE_ERR_INVALID_ARG, "n_bins = %d outside [1, %d]", n_bins, moe::qb_max_bins());
+    return MOE_OK;
+}
+
 struct FfnWs {
     int4* tiles;
     int32_t* tile_start;
@@ -148,6 +171,7 @@ size_t moe_workspace_bytes(const moe_shape_t* shape, int call) {
         case MOE_CALL_PERMUTE: ok(); return permute_ws(shape);
         case MOE_CALL_EXPERT_FFN: ok(); return ffn_ws(shape);
         case MOE_CALL_ROUTE: ok(); return route_ws(shape);
+        case MOE_CALL_AUX_LOSS: ok(); return aux_ws(shape);
         case MOE_CALL_FORWARD: {
             size_t off[kFwdTotal + 1];
             forward_layout(shape, off);
@@ -312,6 +336,66 @@ int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* ro
     hipError_t err = moe::launch_combine(y_rows, row_of, topk_w, shape->T, shape->d, shape->k,
                                          shape->T * shape->k, out, static_cast<hipStream_t>(stream));
     return hip_status(err, "combine launch");
+}
+
+int moe_aux_loss(const moe_shape_t* shape, const float* logits, float* prob_mean, float* aux_loss, void* ws,
+                 size_t ws_bytes, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(logits);
+    MOE_CHECK_PTR(prob_mean);
+    MOE_CHECK_PTR(aux_loss);
+    st = check_ws(ws, ws_bytes, aux_ws(shape));
+    if (st != MOE_OK) return st;
+    hipError_t err = moe::launch_aux_loss(logits, shape->T, shape->E, prob_mean, aux_loss, ws,
+                                          static_cast<hipStream_t>(stream));
+    return hip_status(err, "aux_loss launch");
+}
+
+int moe_qb_route(const moe_shape_t* shape, const float* logits, const float* qb_bias, int32_t* topk_idx,
+                 float* topk_w, float* alpha, void* stream) {
+    int st = check_qb_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(logits);
+    MOE_CHECK_PTR(qb_bias);
+    MOE_CHECK_PTR(topk_idx);
+    MOE_CHECK_PTR(topk_w);
+    MOE_CHECK_PTR(alpha);
+    hipError_t err = moe::launch_qb_select(logits, qb_bias, shape->T, shape->E, shape->k, topk_idx, topk_w, alpha,
+                                           static_cast<hipStream_t>(stream));
+    return hip_status(err, "qb_select launch");
+}
+
+int moe_qb_histogram(const moe_shape_t* shape, const float* logits, const float* alpha, float lo, float width,
+                     int32_t n_bins, int32_t* hist, void* stream) {
+    int st = check_qb_shape(shape);
+    if (st != MOE_OK) return st;
+    st = check_bins(lo, width, n_bins);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_PTR(hist);
+    if (shape->T > 0) {
+        MOE_CHECK_PTR(logits);
+        MOE_CHECK_PTR(alpha);
+    }
+    hipError_t err = moe::launch_qb_histogram(logits, alpha, shape->T, shape->E, lo, width, n_bins, hist,
+                                              static_cast<hipStream_t>(stream));
+    return hip_status(err, "qb_histogram launch");
+}
+
+int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float width, int32_t n_bins,
+                  const float* bias_in, float* bias_out, void* stream) {
+    int st = check_qb_shape(shape);
+    if (st != MOE_OK) return st;
+    st = check_bins(lo, width, n_bins);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_PTR(hist);
+    MOE_CHECK_PTR(bias_in);
+    MOE_CHECK_PTR(bias_out);
+    hipError_t err = moe::launch_qb_update(hist, shape->E, shape->k, n_bins, lo, width, bias_in, bias_out,
+                                           static_cast<hipStream_t>(stream));
+    return hip_status(err, "qb_update launch");
 }
 
 int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,

@@ -154,18 +154,6 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 // exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0): the softmax denominator cancels,
 // so only the k selected logits are exponentiated.
 
-__device__ __forceinline__ uint32_t order_key(float v) {
-    if (v != v) return 0u;     // NaN: below every number
-    if (v == 0.0f) v = 0.0f;   // -0.0 ties +0.0
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t k) {
-    if (k == 0u) return __uint_as_float(0x7fc00000u);
-    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
-}
-
 template <int NPER>
 __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restrict__ logits,
                                                            int64_t T, int E, int k,

@@ -215,3 +215,71 @@ def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, k: int):
     T, d = x.shape
     E, h, _ = w_gate.shape
     return MoEForward(T, d, E, k, h, x.device)(x, w_router, router_bias, w_gate, w_up, w_down)
+
+
+# ------------------------------------------------------------ load balancing
+
+def moe_aux_loss(logits):
+    """(prob_mean [E] f32, aux_loss [1] f32) from f32 logits [T, E]: each expert's
+    batch-mean softmax probability and sum_e (prob_mean[e] - 1/E)^2."""
+    _need(logits, "logits", "f32")
+    dev = logits.device
+    T, E = logits.shape
+    if T == 0:
+        raise ValueError("the aux loss of an empty batch is undefined")
+    s = _lib.shape(T, 128, E, 1, 128)
+    prob_mean = torch.empty(E, dtype=torch.float32, device=dev)
+    aux = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = workspace(s, _lib.MOE_CALL_AUX_LOSS, dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_aux_loss(ctypes.byref(s), _ptr(logits), _ptr(prob_mean), _ptr(aux), _ptr(ws),
+                                         ws.numel(), _stream(dev)))
+    return prob_mean, aux
+
+
+def moe_qb_route(logits, qb_bias, k: int):
+    """Quantile Balancing selection: top-k ids [T,k] i32 of logits + qb_bias, weights [T,k] f32
+    from the unbiased logits, and the cutoff alpha [T] f32 (the (k+1)-th biased score)."""
+    _need(logits, "logits", "f32")
+    dev = logits.device
+    T, E = logits.shape
+    _need(qb_bias, "qb_bias", "f32", (E,), dev)
+    s = _lib.shape(T, 128, E, k, 128)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    alpha = torch.empty(T, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_qb_route(ctypes.byref(s), _ptr(logits), _ptr(qb_bias), _ptr(idx), _ptr(w),
+                                         _ptr(alpha), _stream(dev)))
+    return idx, w, alpha
+
+
+def moe_qb_histogram(logits, alpha, k: int, lo: float, width: float, n_bins: int, out=None):
+    """Per-expert histogram [E, n_bins] i32 of the margins logits - alpha[:, None]."""
+    _need(logits, "logits", "f32")
+    dev = logits.device
+    T, E = logits.shape
+    _need(alpha, "alpha", "f32", (T,), dev)
+    s = _lib.shape(T, 128, E, k, 128)
+    hist = torch.empty((E, n_bins), dtype=torch.int32, device=dev) if out is None else out
+    _need(hist, "hist", "i32", (E, n_bins), dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_qb_histogram(ctypes.byref(s), _ptr(logits), _ptr(alpha), lo, width, n_bins,
+                                             _ptr(hist), _stream(dev)))
+    return hist
+
+
+def moe_qb_update(hist, k: int, lo: float, width: float, bias_in, out=None):
+    """New Quantile Balancing bias [E] f32: minus the (1 - k/E)-quantile of each histogram row
+    (rows with no counts keep bias_in). `out` may be bias_in itself."""
+    _need(hist, "hist", "i32")
+    dev = hist.device
+    E, n_bins = hist.shape
+    _need(bias_in, "bias_in", "f32", (E,), dev)
+    bias_out = torch.empty(E, dtype=torch.float32, device=dev) if out is None else out
+    _need(bias_out, "bias_out", "f32", (E,), dev)
+    s = _lib.shape(0, 128, E, k, 128)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_qb_update(ctypes.byref(s), _ptr(hist), lo, width, n_bins, _ptr(bias_in),
+                                          _ptr(bias_out), _stream(dev)))
+    return bias_out

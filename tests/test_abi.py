@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
-              "moe_workspace_bytes", "moe_status_str", "moe_last_error"]:
+              "moe_workspace_bytes", "moe_status_str", "moe_last_error", "moe_aux_loss",
+              "moe_qb_route", "moe_qb_histogram", "moe_qb_update"]:
         assert n in names
 
 
@@ -50,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 3
+    assert L.moe_abi_version() == lib.ABI_VERSION == 4
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -151,3 +152,34 @@ def test_zero_tokens_is_a_noop(lib):
     assert L.moe_combine(ctypes.byref(s), None, None, None, None, None) == 0
     assert L.moe_forward(ctypes.byref(s), None, None, None, None, None, None, None, None, 0, None) == 0
     assert L.moe_expert_ffn(ctypes.byref(s), None, None, None, None, None, None, None, None, None, 0, None) == 0
+
+
+def test_balance_calls_reject_bad_arguments(lib):
+    L = lib.lib
+    a = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 4)
+    s = _shape(lib)
+    f = ctypes.c_float
+    # Quantile Balancing needs k < E and k <= 63
+    for bad in (dict(k=8, E=8), dict(E=100, k=64)):
+        sb = _shape(lib, **bad)
+        assert L.moe_qb_route(ctypes.byref(sb), a, a, a, a, a, None) == 1
+        assert b"k < E" in L.moe_last_error()
+        assert L.moe_qb_histogram(ctypes.byref(sb), a, a, f(-8.0), f(0.01), 1000, a, None) == 1
+        assert L.moe_qb_update(ctypes.byref(sb), a, f(-8.0), f(0.01), 1000, a, a, None) == 1
+    assert L.moe_qb_route(ctypes.byref(s), a, None, a, a, a, None) == 1
+    assert L.moe_qb_route(ctypes.byref(s), a, a, a, a, mis, None) == 1
+    for lo, width, nb in [(float("nan"), 0.01, 10), (0.0, 0.0, 10), (0.0, -1.0, 10), (0.0, float("inf"), 10),
+                          (float("-inf"), 1.0, 10), (0.0, 0.01, 0), (0.0, 0.01, 4097)]:
+        assert L.moe_qb_histogram(ctypes.byref(s), a, a, f(lo), f(width), nb, a, None) == 1
+        assert L.moe_qb_update(ctypes.byref(s), a, f(lo), f(width), nb, a, a, None) == 1
+    assert L.moe_qb_histogram(ctypes.byref(s), a, a, f(0.0), f(0.01), 100, None, None) == 1
+    assert L.moe_qb_update(ctypes.byref(s), a, f(0.0), f(0.01), 100, None, a, None) == 1
+    assert L.moe_aux_loss(ctypes.byref(s), None, a, a, a, 1 << 20, None) == 1
+    need = lib.workspace_bytes(s, lib.MOE_CALL_AUX_LOSS)
+    assert need >= 4 * GOOD["E"] + 8 * GOOD["E"] and need % 256 == 0
+    assert L.moe_aux_loss(ctypes.byref(s), a, a, a, a, need - 1, None) == 3
+    assert L.moe_aux_loss(ctypes.byref(s), a, a, a, None, need, None) == 3
+    s0 = _shape(lib, T=0)
+    assert L.moe_aux_loss(ctypes.byref(s0), None, None, None, None, 0, None) == 0
+    assert L.moe_qb_route(ctypes.byref(s0), None, None, None, None, None, None) == 0
