@@ -62,7 +62,7 @@ def latent_forward(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, e
 
     x [T, d]; w_router [E, d]; bias [E] or None; w_proj_down [l, d];
     w_gate, w_up [E, h, l]; w_down [E, l, h]; gain [l]; w_proj_up [d, l];
-    shared_gate, shared_up [S, hs, d]; shared_down [S, d, hs] (S may be 0).
+    shared_gate, shared_up [S, hs, d]; shared_down [S, d, hs] (S may be 0, or the three None).
     `logits` replaces the oracle's own gate logits (e.g. the device's).
     """
     X = _m.f64(x)
@@ -79,7 +79,8 @@ def latent_forward(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, e
     if bf16_operands:
         r = bf16_round(r)
     up = r @ _m.f64(w_proj_up).T
-    shared = [dense_swiglu(X, shared_gate[s], shared_up[s], shared_down[s]) for s in range(len(shared_gate))]
+    n_shared = 0 if shared_gate is None else len(shared_gate)
+    shared = [dense_swiglu(X, shared_gate[s], shared_up[s], shared_down[s]) for s in range(n_shared)]
     out = up.copy()
     for y in shared:
         out = out + y
