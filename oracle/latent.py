@@ -21,9 +21,10 @@ Readings (also listed in the design notes):
   * RMSNorm(u) = g * u / sqrt(mean_j u_j^2 + eps), with a gain g in R^l;
   * every expert (routed in R^l, shared in R^d) is SwiGLU without biases;
   * activations that enter a matrix product are bfloat16 (the layer's input
-    dtype): z and RMSNorm(u) are rounded to bfloat16 (round to nearest even)
-    before their products when `bf16_operands` is set, as the device does;
-    everything else is float64.
+    dtype): z, every expert's SwiGLU activation H and RMSNorm(u) are rounded
+    to bfloat16 (round to nearest even, through float32) before their products
+    when `bf16_operands` is set, as the device does; everything else is
+    float64.
 """
 from __future__ import annotations
 
@@ -51,9 +52,38 @@ def rmsnorm(u, gain, eps: float) -> np.ndarray:
     return U / np.sqrt(ms + eps) * g
 
 
-def dense_swiglu(X, w_gate, w_up, w_down):
+def swiglu_rows(X, w_gate, w_up, w_down, bf16_operands: bool):
+    """One SwiGLU FFN on the rows of X (weights [h, d], [h, d], [d, h]):
+    H = silu(X Wg^T) * (X Wu^T), bf16-rounded when bf16_operands; Y = H Wd^T. Returns (H, Y)."""
+    X = _m.f64(X)
+    H = _m.silu(X @ _m.f64(w_gate).T) * (X @ _m.f64(w_up).T)
+    if bf16_operands:
+        H = bf16_round(H)
+    return H, H @ _m.f64(w_down).T
+
+
+def dense_swiglu(X, w_gate, w_up, w_down, bf16_operands: bool = False):
     """One SwiGLU FFN applied to every row of X (weights [h, d], [h, d], [d, h])."""
-    return _m.expert_swiglu(X, w_gate, w_up, w_down)[1]
+    return swiglu_rows(X, w_gate, w_up, w_down, bf16_operands)[1]
+
+
+def routed_experts(z_rows, offsets, w_gate, w_up, w_down, bf16_operands: bool):
+    """Expert e on its rows offsets[e] .. offsets[e+1]-1 of z_rows (rows of experts with no
+    rows are skipped). Returns (H, Y) with NaN in rows no expert computed."""
+    Z = _m.f64(z_rows)
+    off = _m._int(offsets)
+    H = Y = None
+    for e in range(off.shape[0] - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        He, Ye = swiglu_rows(Z[lo:hi], w_gate[e], w_up[e], w_down[e], bf16_operands)
+        if H is None:
+            H = np.full((Z.shape[0], He.shape[1]), np.nan)
+            Y = np.full((Z.shape[0], Ye.shape[1]), np.nan)
+        H[lo:hi] = He
+        Y[lo:hi] = Ye
+    return H, Y
 
 
 def latent_forward(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, eps, w_proj_up,
@@ -73,14 +103,14 @@ def latent_forward(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, e
     z = X @ _m.f64(w_proj_down).T
     if bf16_operands:
         z = bf16_round(z)
-    H, Y = _m.expert_ffn(z[row_src], offsets, w_gate, w_up, w_down)
+    H, Y = routed_experts(z[row_src], offsets, w_gate, w_up, w_down, bf16_operands)
     u = _m.combine(Y, row_of, w)
     r = rmsnorm(u, gain, eps)
     if bf16_operands:
         r = bf16_round(r)
     up = r @ _m.f64(w_proj_up).T
     n_shared = 0 if shared_gate is None else len(shared_gate)
-    shared = [dense_swiglu(X, shared_gate[s], shared_up[s], shared_down[s]) for s in range(n_shared)]
+    shared = [dense_swiglu(X, shared_gate[s], shared_up[s], shared_down[s], bf16_operands) for s in range(n_shared)]
     out = up.copy()
     for y in shared:
         out = out + y

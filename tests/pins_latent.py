@@ -144,8 +144,9 @@ def pin_latent_up_projection_linear(lat):
 
 
 def pin_latent_rounding_points(lat):
-    """With bf16 operands, z and RMSNorm(u) are bf16 values (fixed by rounding) and the
-    result stays within bf16 rounding of the unrounded layer."""
+    """With bf16 operands, z, the experts' H and RMSNorm(u) are bf16 values (fixed by
+    rounding), the routed experts' rows equal the plain layer's expert FFN on bf16
+    H by torch float64, and the result stays near the unrounded layer."""
     r = _rng(5)
     T, d, l, E, k, h = 10, 8, 4, 5, 2, 6
     x = r.standard_normal((T, d))
@@ -155,9 +156,19 @@ def pin_latent_rounding_points(lat):
     none = np.zeros((0, 2, d)), np.zeros((0, 2, d)), np.zeros((0, d, 2))
     a = lat.latent_forward(x, *args, *none, k=k, bf16_operands=True)
     b = lat.latent_forward(x, *args, *none, k=k, bf16_operands=False)
-    for name in ("z", "r"):
-        _close(lat.bf16_round(a[name]), a[name], 0.0, f"{name} is bf16")
+    for name in ("z", "r", "H"):
+        v = a[name][~np.isnan(a[name])]
+        _close(lat.bf16_round(v), v, 0.0, f"{name} is bf16")
     _close(a["z"], b["z"], 2.0 ** -8 * np.abs(b["z"]).max(), "z rounding")
+    # one routed expert by torch: H = bf16(silu(z Wg^T) * z Wu^T), Y = H Wd^T
+    off, row_src = a["offsets"], a["row_src"]
+    e = int(np.argmax(np.diff(off)))
+    Z = torch.as_tensor(a["z"][row_src[off[e]:off[e + 1]]])
+    wg, wu, wd = (torch.as_tensor(np.asarray(v[e], dtype=np.float64)) for v in args[3:6])
+    Ht = (torch.nn.functional.silu(Z @ wg.T) * (Z @ wu.T)).float().to(torch.bfloat16).double()
+    _close(a["H"][off[e]:off[e + 1]], Ht.numpy(), 0.0, "routed H")
+    _close(a["Y"][off[e]:off[e + 1]], (Ht @ wd.T).numpy(), 1e-12, "routed Y")
+    assert np.abs(a["out"] - b["out"]).max() < 0.05 * np.abs(b["out"]).max()
     assert not np.array_equal(a["out"], b["out"])
 
 
