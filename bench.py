@@ -46,7 +46,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill",
-                    help="named workload (prefill is the headline: T=8192 d=7168 E=256 k=4 h=2048)")
+                    help="named workload (prefill is the headline: T=8192 d=7168 E=256 k=4 h=2048; "
+                         "'latent' times the Stable LatentMoE layer instead)")
     ap.add_argument("--cpu-experts", type=int, default=128,
                     help="experts the CPU oracle runs in its bounded sample (0 = skip the CPU baseline)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -233,6 +234,112 @@ def cpu_baseline(inp, cfg, n_experts):
     }
 
 
+def latent_bench(args, dev, note):
+    """The Stable LatentMoE layer: K calls of moe_latent_forward on one stream."""
+    import torch
+
+    from synthetic import LATENT_CONFIGS, make_latent_inputs
+    from sparse_mixture_experts_fp32_amd import _lib as lib
+
+    cfg = LATENT_CONFIGS[args.workload]
+    T, d, l, E, k, h, S, hs = cfg.T, cfg.d, cfg.l, cfg.E, cfg.k, cfg.h, cfg.n_shared, cfg.h_shared
+    inp = make_latent_inputs(cfg, device=dev, progress=lambda n: note(f"drew {n} of {E} experts' weights"))
+    torch.cuda.synchronize()
+    note("inputs ready")
+    shape = lib.latent_shape(T, d, l, E, k, h, S, hs)
+    ws = torch.empty(lib.latent_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    args_c = [ctypes.byref(shape), P(inp.x), P(inp.w_router), None, P(inp.w_proj_down), P(inp.w_gate), P(inp.w_up),
+              P(inp.w_down), P(inp.rms_gain), ctypes.c_float(inp.rms_eps), P(inp.w_proj_up), P(inp.shared_gate),
+              P(inp.shared_up), P(inp.shared_down), P(out), P(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
+
+    def step():
+        lib.check(lib.lib.moe_latent_forward(*args_c))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    note(f"{args.warmup} warmup steps done")
+    K = args.steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(K):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    gpu_ms = start.elapsed_time(stop) / K
+    note(f"{K} timed steps done")
+    n = T * k
+    flops = {"router": 2.0 * T * d * E, "down_projection": 2.0 * T * d * l, "routed_gate_up": 4.0 * n * l * h,
+             "routed_down": 2.0 * n * l * h, "up_projection": 2.0 * T * l * d, "shared": 6.0 * S * T * d * hs}
+    total = sum(flops.values())
+    tflops = total / (gpu_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Stable LatentMoE, T={T} d={d} l={l} E={E} top-{k} h={h}, "
+                               f"{S} shared experts of width {hs}, fp32 gate",
+                   "T": T, "d": d, "l": l, "E": E, "k": k, "h": h, "n_shared": S, "h_shared": hs, "seed": cfg.seed},
+        "gpu_ms_per_step": gpu_ms,
+        "flops": flops,
+        "roofline": {"kernel": "whole LatentMoE step (every kernel of moe_latent_forward)", "bound": "mfma",
+                     "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "algorithmic_flops": total},
+    }
+    if args.cpu_experts > 0:
+        note("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = latent_cpu_baseline(inp, cfg, n_tokens=16)
+    return result
+
+
+def latent_cpu_baseline(inp, cfg, n_tokens):
+    """The LatentMoE oracle on the host cores for n_tokens evenly spaced tokens (every
+    step of the layer for those tokens, the experts they route to copied to host
+    memory first), scaled to the whole batch."""
+    import numpy as np
+
+    import oracle.latent as lat
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count()
+    sample = np.linspace(0, cfg.T - 1, n_tokens).astype(np.int64)
+    x = inp.x[sample].cpu()
+    host = {name: getattr(inp, name).cpu() for name in ("w_router", "w_proj_down", "rms_gain", "w_proj_up",
+                                                        "shared_gate", "shared_up", "shared_down")
+            if getattr(inp, name) is not None}
+    logits = (x.double() @ host["w_router"].double().T).numpy()
+    need = sorted({int(e) for e in np.argsort(-logits, axis=1)[:, :cfg.k + 2].ravel()})
+
+    class Experts(dict):
+        def __init__(self, t):
+            super().__init__({e: t[e].cpu() for e in need})
+            self.t = t
+
+        def __missing__(self, e):
+            self[e] = self.t[e].cpu()
+            return self[e]
+
+    wg, wu, wd = Experts(inp.w_gate), Experts(inp.w_up), Experts(inp.w_down)
+    t0 = time.perf_counter()
+    lat.latent_forward(x, host["w_router"], None, host["w_proj_down"], wg, wu, wd, host["rms_gain"], inp.rms_eps,
+                       host["w_proj_up"], host.get("shared_gate"), host.get("shared_up"), host.get("shared_down"),
+                       k=cfg.k)
+    sec = time.perf_counter() - t0
+    layer_s = sec * cfg.T / n_tokens
+    return {"value": cfg.T / layer_s, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"{cfg.name} workload, float64 numpy oracle of the whole LatentMoE layer for {n_tokens} of "
+                       f"{cfg.T} tokens (their experts copied to host memory beforehand); {sec:.1f} s measured, "
+                       f"scaled by {cfg.T / n_tokens:.0f} to {layer_s:.0f} s per layer")}
+
+
 def measured_traffic(workload):
     """HBM bytes per gate/up launch from the committed counter record, or None if the kernel changed since."""
     import hashlib
@@ -261,15 +368,19 @@ def main():
 
     import torch
 
-    from synthetic import CONFIGS, make_inputs
+    from synthetic import CONFIGS, LATENT_CONFIGS, make_inputs
     from sparse_mixture_experts_fp32_amd import _lib as lib
     from sparse_mixture_experts_fp32_amd import MoEForward
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
+    if args.workload in LATENT_CONFIGS:
+        note = lambda msg: print(f"[bench] {args.workload}: {msg}", file=sys.stderr, flush=True)  # noqa: E731
+        print(json.dumps(latent_bench(args, dev, note)), flush=True)
+        return
+    cfg = CONFIGS[args.workload]
     def progress(n):
         print(f"[bench] {cfg.name}: drew {n} of {cfg.E} experts' weights", file=sys.stderr, flush=True)
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -290,6 +290,81 @@ int moe_qb_histogram(const moe_shape_t* shape, const float* logits, const float*
                      float width, int32_t n_bins, int32_t* hist, void* stream);
 int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float width,
                   int32_t n_bins, const float* bias_in, float* bias_out, void* stream);
+
+/*
+ * ---------------------------------------------------------------- LatentMoE
+ * The Stable LatentMoE layer ("Kimi K3: Open Frontier Intelligence", section
+ * "Operational Execution Flow: From Native Multimodal Inputs to Sparse Channel
+ * Activations"): shared experts read x at full width, while the routed path
+ * projects x down to a latent z, routes z through the k experts the gate picks
+ * (from x), sums them into u, normalises u with an RMSNorm and projects back up:
+ *   out = W_up_proj RMSNorm(u) + sum_s SharedExpert_s(x),
+ *   u = sum_{j<k} w[t, j] E_{idx[t, j]}(z),  z = W_down_proj x,
+ *   RMSNorm(u) = g * u / sqrt(mean u^2 + eps).
+ * Every expert is SwiGLU. z and RMSNorm(u) are rounded to bf16 (they are
+ * matrix-core operands); u, the expert outputs and out are float32.
+ */
+typedef struct moe_latent_shape {
+    int64_t T;        /* tokens */
+    int32_t d;        /* model width: x, out, shared experts (multiple of 128) */
+    int32_t l;        /* latent width of the routed path (multiple of 128, <= 8192) */
+    int32_t E;        /* routed experts, acting on R^l */
+    int32_t k;        /* experts per token */
+    int32_t h;        /* hidden width of a routed expert (multiple of 128) */
+    int32_t n_shared; /* shared experts, 0 .. 8 */
+    int32_t h_shared; /* hidden width of a shared expert (multiple of 128; unused when n_shared = 0) */
+} moe_latent_shape_t;
+
+/* Intermediates moe_latent_forward leaves in its workspace (moe_latent_ws_offset). */
+typedef enum moe_latent_slot {
+    MOE_LAT_LOGITS = 0,         /* [T, E] float32 */
+    MOE_LAT_TOPK_IDX = 1,       /* [T, k] int32 */
+    MOE_LAT_TOPK_W = 2,         /* [T, k] float32 */
+    MOE_LAT_EXPERT_OFFSETS = 3, /* [E + 1] int32 */
+    MOE_LAT_ROW_OF = 4,         /* [T, k] int32 */
+    MOE_LAT_ROW_SRC = 5,        /* [T * k] int32 */
+    MOE_LAT_Z = 6,              /* [T, l] bf16: x W_down_proj^T */
+    MOE_LAT_H = 7,              /* [T * k, h] bf16: routed SwiGLU activations */
+    MOE_LAT_Y = 8,              /* [T * k, l] float32: routed expert outputs */
+    MOE_LAT_R = 9,              /* [T, l] bf16: RMSNorm(u) */
+    MOE_LAT_SHARED_H = 10,      /* [n_shared * T, h_shared] bf16 */
+    MOE_LAT_SHARED_Y = 11,      /* [n_shared * T, d] float32: shared expert s on rows s*T .. s*T + T - 1 */
+    MOE_LAT_NUM_SLOTS = 12
+} moe_latent_slot_t;
+
+/* Workspace bytes of moe_latent_forward (0 with moe_last_error() set on a bad shape). */
+size_t moe_latent_workspace_bytes(const moe_latent_shape_t* shape);
+int moe_latent_ws_offset(const moe_latent_shape_t* shape, int slot, size_t* offset);
+
+/*
+ * moe_latent_forward -- the whole LatentMoE layer on one stream.
+ *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL
+ *  w_proj_down [l, d] bf16; w_gate, w_up [E, h, l] bf16; w_down [E, l, h] bf16
+ *  rms_gain [l] f32; rms_eps >= 0 (finite); w_proj_up [d, l] bf16
+ *  shared_gate, shared_up [n_shared, h_shared, d] bf16; shared_down [n_shared, d, h_shared] bf16
+ *    (all three may be NULL when n_shared = 0)
+ *  out [T, d] float32 (written)
+ *  ws, ws_bytes  workspace of at least moe_latent_workspace_bytes(shape)
+ * Sums: u in slot order; out = ((W_up_proj r) + shared_0) + shared_1 ...
+ */
+int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                       const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                       const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                       const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                       const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine_rmsnorm -- the routed sum followed by the RMSNorm, in one pass
+ * (same page and section): u[t] = sum_j topk_w[t, j] y_rows[row_of[t, j]]
+ * (float32, slot order, as moe_combine), r[t] = bf16(u[t] / sqrt(mean u[t]^2 + eps) * gain).
+ *  shape->d is the row width (the latent width l, <= 8192)
+ *  y_rows [T * k, d] f32; row_of [T, k] int32 (-1 entries skipped); topk_w [T, k] f32;
+ *  gain [d] f32; eps >= 0 (finite)  (all read)
+ *  u_out [T, d] f32 (written; may be NULL); r_out [T, d] bf16 (written)
+ */
+int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of,
+                        const float* topk_w, const float* gain, float eps, float* u_out, uint16_t* r_out,
+                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,13 +24,21 @@ MOE_CALL_FORWARD = 2
 MOE_CALL_ROUTE = 3
 MOE_CALL_AUX_LOSS = 4
 
+LAT_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "z", "h_act", "y_rows", "r",
+             "shared_h", "shared_y"]
 FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("h", ctypes.c_int32)]
+
+
+class MoeLatentShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("l", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("h", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("h_shared", ctypes.c_int32)]
 
 
 class MoEError(RuntimeError):
@@ -45,6 +53,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     S = ctypes.POINTER(MoeShape)
+    LS = ctypes.POINTER(MoeLatentShape)
     sig = {
         "moe_abi_version": (ctypes.c_int, []),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -63,6 +72,11 @@ def _load():
         "moe_qb_route": (ctypes.c_int, [S, P, P, P, P, P, P]),
         "moe_qb_histogram": (ctypes.c_int, [S, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32, P, P]),
         "moe_qb_update": (ctypes.c_int, [S, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32, P, P, P]),
+        "moe_latent_workspace_bytes": (ctypes.c_size_t, [LS]),
+        "moe_latent_ws_offset": (ctypes.c_int, [LS, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_latent_forward": (ctypes.c_int, [LS, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
+                                              ctypes.c_size_t, P]),
+        "moe_combine_rmsnorm": (ctypes.c_int, [S, P, P, P, P, ctypes.c_float, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -97,4 +111,22 @@ def workspace_bytes(s: MoeShape, call: int) -> int:
 def forward_ws_offset(s: MoeShape, slot: int) -> int:
     off = ctypes.c_size_t(0)
     check(lib.moe_forward_ws_offset(ctypes.byref(s), slot, ctypes.byref(off)))
+    return off.value
+
+
+def latent_shape(T: int, d: int, l: int, E: int, k: int, h: int, n_shared: int, h_shared: int) -> MoeLatentShape:
+    return MoeLatentShape(T, d, l, E, k, h, n_shared, h_shared)
+
+
+def latent_workspace_bytes(s: MoeLatentShape) -> int:
+    n = lib.moe_latent_workspace_bytes(ctypes.byref(s))
+    err = lib.moe_last_error().decode()
+    if n == 0 and err:
+        raise MoEError(MOE_ERR_INVALID_ARG, err)
+    return n
+
+
+def latent_ws_offset(s: MoeLatentShape, slot: int) -> int:
+    off = ctypes.c_size_t(0)
+    check(lib.moe_latent_ws_offset(ctypes.byref(s), slot, ctypes.byref(off)))
     return off.value

@@ -163,7 +163,7 @@ __device__ __forceinline__ void mfma_step(f32x4 (&acc)[kNB][kMBW], const uint16_
 // Every load and LDS store in the K loop is unconditional: rows past M re-read
 // row M - 1 and prefetch indices are clamped to the last K step (a repeated
 // step is loaded but never used).
-template <class C, bool kGated, int kMB>
+template <class C, bool kGated, bool kBf16, int kMB>
 __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restrict__ A,
                                          const int32_t* __restrict__ A_rows, int64_t A_nrows, int64_t row0, int M,
                                          const uint16_t* const (&wb)[C::kNB], bool wave_on, int N, int K, int wm,
@@ -274,7 +274,11 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
                     const float g = acc[c][i][q], u = acc[kNB / 2 + c][i][q];
                     crow[16 * c] = f32_to_bf16_bits(g / (1.0f + __expf(-g)) * u);
                 }
-            } else {       // Y row: float32
+            } else if (kBf16) {  // plain product rounded to bf16 (an operand of a later pass)
+                uint16_t* crow = static_cast<uint16_t*>(Cout) + (row0 + r) * N + n_wave + frag_row;
+#pragma unroll
+                for (int b = 0; b < kNB; ++b) crow[16 * b] = f32_to_bf16_bits(acc[b][i][q]);
+            } else {             // Y row: float32
                 float* crow = static_cast<float*>(Cout) + (row0 + r) * N + n_wave + frag_row;
 #pragma unroll
                 for (int b = 0; b < kNB; ++b) crow[16 * b] = acc[b][i][q];
@@ -286,7 +290,7 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
 // One workgroup per CU is the design point (LDS tile and register budget), so the
 // register allocator is told that occupancy is fixed and may spend registers on
 // keeping loads in flight rather than on reaching a higher wave count.
-template <class C, bool kGated>
+template <class C, bool kGated, bool kBf16>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, C::kWaves / 4)))
 void grouped_ffn_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ A_rows, int64_t A_nrows,
@@ -338,8 +342,8 @@ void grouped_ffn_kernel(
     const int mb = min(C::kMaxMB, ((M + 16 * kStepMB - 1) / (16 * kStepMB)) * kStepMB);
 #define MOE_TILE(NB)                                                                                   \
     if (mb == (NB)) {                                                                                  \
-        ffn_tile<C, kGated, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, A_rows, A_nrows, row0, M, wb,    \
-                                                                   wave_on, N, K, wm, n_wave, Cout);   \
+        ffn_tile<C, kGated, kBf16, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, A_rows, A_nrows, row0, M, \
+                                                                          wb, wave_on, N, K, wm, n_wave, Cout); \
         return;                                                                                        \
     }
     MOE_TILE(kStepMB)
@@ -362,7 +366,7 @@ static int max_tiles_for(int64_t n_rows, int E, int bm) {
     return static_cast<int>(t);
 }
 
-template <class C, bool kGated>
+template <class C, bool kGated, bool kBf16 = false>
 hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows, const int4* tiles,
                       const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* W0, const uint16_t* W1, int N,
                       int K, void* Cout, hipStream_t stream) {
@@ -372,7 +376,7 @@ hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows,
     const int n_tiles = (N + cols_wg - 1) / cols_wg;
     const int slots = (max_tiles_for(n_rows, E, C::kBM) + kXcds - 1) / kXcds;
     const int64_t grid = static_cast<int64_t>(kXcds) * slots * n_tiles;
-    hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
+    hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated, kBf16>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
                        stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
     return hipGetLastError();
 }
@@ -384,7 +388,9 @@ hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows,
 // steps ahead; the down pass (K = h, a quarter as deep) measured best one ahead.
 using GateUpCfg = GemmCfg<1, 8, 2, 64, 12, true, 16>;
 using DownCfg = GemmCfg<1, 8, 2, 64, 12, false, 16>;
-static_assert(GateUpCfg::kBM == DownCfg::kBM, "both passes share one m-tile list");
+// plain products with a deep K (the latent projections: K = d or l)
+using DenseCfg = GemmCfg<1, 8, 2, 64, 12, true, 16>;
+static_assert(GateUpCfg::kBM == DownCfg::kBM && DenseCfg::kBM == DownCfg::kBM, "all passes share one m-tile size");
 
 int ffn_tile_rows() { return GateUpCfg::kBM; }
 
@@ -408,6 +414,16 @@ hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* 
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream) {
     return launch_ffn<DownCfg, false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
                                       y_rows, stream);
+}
+
+hipError_t launch_dense(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
+                        bool bf16_out, hipStream_t stream) {
+    if (bf16_out)
+        return launch_ffn<DenseCfg, false, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K,
+                                                 c, stream);
+    return launch_ffn<DenseCfg, false, false>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c,
+                                              stream);
 }
 
 }  // namespace moe

@@ -44,4 +44,16 @@ size_t aux_ws_bytes(int64_t T, int E);
 hipError_t launch_aux_loss(const float* logits, int64_t T, int E, float* prob_mean, float* aux_loss, void* ws,
                            hipStream_t stream);
 
+hipError_t launch_dense(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
+                        bool bf16_out, hipStream_t stream);
+
+int combine_rmsnorm_max_width();
+hipError_t launch_combine_rmsnorm(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T, int l,
+                                  int k, int64_t n_rows, const float* gain, float eps, float* u_out,
+                                  uint16_t* r_out, hipStream_t stream);
+hipError_t launch_latent_maps(int64_t T, int S, int32_t* dense_off, int32_t* shared_off, int32_t* shared_rows,
+                              hipStream_t stream);
+hipError_t launch_add_shared(float* out, const float* ys, int64_t T, int d, int S, hipStream_t stream);
+
 }  // namespace moe

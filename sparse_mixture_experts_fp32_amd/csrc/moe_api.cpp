@@ -117,6 +117,13 @@ int check_bins(float lo, float width, int32_t n_bins) {
     return MOE_OK;
 }
 
+// Grouped-GEMM workspace for n_rows rows over E groups: m-tile list, then first m-tile per group.
+size_t ffn_ws_rows(int64_t n_rows, int E) {
+    if (n_rows == 0) return 0;
+    return align_up(sizeof(int4) * static_cast<size_t>(moe::ffn_max_tiles(n_rows, E))) +
+           align_up(sizeof(int32_t) * (static_cast<size_t>(E) + 1));
+}
+
 struct FfnWs {
     int4* tiles;
     int32_t* tile_start;
@@ -125,6 +132,66 @@ struct FfnWs {
 FfnWs ffn_carve(const moe_shape_t* s, void* ws) {
     char* b = static_cast<char*>(ws);
     return FfnWs{reinterpret_cast<int4*>(b), reinterpret_cast<int32_t*>(b + ffn_tiles_bytes(s))};
+}
+
+FfnWs ffn_carve_rows(int64_t n_rows, int E, void* ws) {
+    char* b = static_cast<char*>(ws);
+    const size_t tiles = align_up(sizeof(int4) * static_cast<size_t>(moe::ffn_max_tiles(n_rows, E)));
+    return FfnWs{reinterpret_cast<int4*>(b), reinterpret_cast<int32_t*>(b + tiles)};
+}
+
+// ------------------------------------------------------------ LatentMoE
+
+int check_latent_shape(const moe_latent_shape_t* s) {
+    if (s == nullptr) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+    // the routed path is a plain routed layer of width l
+    const moe_shape_t r{s->T, s->l, s->E, s->k, s->h};
+    int st = check_shape(&r);
+    if (st != MOE_OK) return st;
+    if (s->d < 128 || s->d % 128 != 0 || s->d > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "d = %d is not a positive multiple of 128 (<= 2^20)", s->d);
+    if (s->l > moe::combine_rmsnorm_max_width())
+        return fail(MOE_ERR_UNSUPPORTED, "l = %d > %d", s->l, moe::combine_rmsnorm_max_width());
+    if (s->n_shared < 0 || s->n_shared > 8)
+        return fail(MOE_ERR_INVALID_ARG, "n_shared = %d outside [0, 8]", s->n_shared);
+    if (s->n_shared > 0 && (s->h_shared < 128 || s->h_shared % 128 != 0 || s->h_shared > (1 << 20)))
+        return fail(MOE_ERR_INVALID_ARG, "h_shared = %d is not a positive multiple of 128 (<= 2^20)", s->h_shared);
+    if (s->T * static_cast<int64_t>(s->n_shared) >= (int64_t(1) << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "n_shared * T >= 2^31");
+    return MOE_OK;
+}
+
+// slots: the public intermediates, then the permute scratch, the routed / dense /
+// shared tile lists, the row maps and the router's weight parts
+constexpr int kLatPermuteWs = MOE_LAT_NUM_SLOTS, kLatFfnWs = MOE_LAT_NUM_SLOTS + 1,
+              kLatDenseWs = MOE_LAT_NUM_SLOTS + 2, kLatSharedWs = MOE_LAT_NUM_SLOTS + 3,
+              kLatMaps = MOE_LAT_NUM_SLOTS + 4, kLatRouteWs = MOE_LAT_NUM_SLOTS + 5,
+              kLatTotal = MOE_LAT_NUM_SLOTS + 6;
+
+int latent_groups(const moe_latent_shape_t* s) { return s->n_shared > 0 ? s->n_shared : 1; }
+
+// row maps: dense offsets [2], shared offsets [S + 1], shared rows [S * T]
+size_t maps_shared_off(const moe_latent_shape_t*) { return align_up(2 * sizeof(int32_t)); }
+size_t maps_shared_rows(const moe_latent_shape_t* s) {
+    return maps_shared_off(s) + align_up(sizeof(int32_t) * (static_cast<size_t>(s->n_shared) + 1));
+}
+
+void latent_layout(const moe_latent_shape_t* s, size_t off[kLatTotal + 1]) {
+    const size_t T = static_cast<size_t>(s->T), E = s->E, k = s->k, d = s->d, l = s->l, h = s->h;
+    const size_t S = static_cast<size_t>(s->n_shared), hs = s->n_shared > 0 ? s->h_shared : 0;
+    const moe_shape_t r{s->T, s->l, s->E, s->k, s->h};
+    const moe_shape_t g{s->T, s->d, s->E, s->k, s->h};  // the router reads x (width d)
+    const size_t sizes[kLatTotal] = {
+        4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k, 2 * T * l, 2 * T * k * h,
+        4 * T * k * l, 2 * T * l, 2 * S * T * hs, 4 * S * T * d,
+        permute_ws(&r), ffn_ws(&r), ffn_ws_rows(s->T, 1), ffn_ws_rows(s->T * s->n_shared, latent_groups(s)),
+        maps_shared_rows(s) + 4 * S * T, route_ws(&g)};
+    size_t at = 0;
+    for (int i = 0; i < kLatTotal; ++i) {
+        off[i] = at;
+        at += align_up(sizes[i]);
+    }
+    off[kLatTotal] = at;
 }
 
 // Byte offsets of every slot of moe_forward's workspace; after the public slots
@@ -448,6 +515,140 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     if (err != hipSuccess) return hip_status(err, "down launch");
     err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
     return hip_status(err, "combine launch");
+}
+
+size_t moe_latent_workspace_bytes(const moe_latent_shape_t* shape) {
+    if (check_latent_shape(shape) != MOE_OK) return 0;
+    size_t off[kLatTotal + 1];
+    latent_layout(shape, off);
+    ok();
+    return off[kLatTotal];
+}
+
+int moe_latent_ws_offset(const moe_latent_shape_t* shape, int slot, size_t* offset) {
+    int st = check_latent_shape(shape);
+    if (st != MOE_OK) return st;
+    if (slot < 0 || slot >= MOE_LAT_NUM_SLOTS) return fail(MOE_ERR_INVALID_ARG, "unknown slot %d", slot);
+    if (offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "offset is NULL");
+    size_t off[kLatTotal + 1];
+    latent_layout(shape, off);
+    *offset = off[slot];
+    return ok();
+}
+
+int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of, const float* topk_w,
+                        const float* gain, float eps, float* u_out, uint16_t* r_out, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->d > moe::combine_rmsnorm_max_width())
+        return fail(MOE_ERR_UNSUPPORTED, "row width %d > %d", shape->d, moe::combine_rmsnorm_max_width());
+    if (!std::isfinite(eps) || eps < 0.f) return fail(MOE_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(y_rows);
+    MOE_CHECK_PTR(row_of);
+    MOE_CHECK_PTR(topk_w);
+    MOE_CHECK_PTR(gain);
+    if (u_out != nullptr && !aligned16(u_out)) return fail(MOE_ERR_INVALID_ARG, "u_out is not 16-byte aligned");
+    MOE_CHECK_PTR(r_out);
+    hipError_t err = moe::launch_combine_rmsnorm(y_rows, row_of, topk_w, shape->T, shape->d, shape->k,
+                                                 shape->T * shape->k, gain, eps, u_out, r_out,
+                                                 static_cast<hipStream_t>(stream));
+    return hip_status(err, "combine_rmsnorm launch");
+}
+
+int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                       const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                       const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                       const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                       const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_latent_shape(shape);
+    if (st != MOE_OK) return st;
+    if (!std::isfinite(rms_eps) || rms_eps < 0.f) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(x);
+    MOE_CHECK_PTR(w_router);
+    if (router_bias != nullptr && !aligned16(router_bias))
+        return fail(MOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+    MOE_CHECK_PTR(w_proj_down);
+    MOE_CHECK_PTR(w_gate);
+    MOE_CHECK_PTR(w_up);
+    MOE_CHECK_PTR(w_down);
+    MOE_CHECK_PTR(rms_gain);
+    MOE_CHECK_PTR(w_proj_up);
+    if (shape->n_shared > 0) {
+        MOE_CHECK_PTR(shared_gate);
+        MOE_CHECK_PTR(shared_up);
+        MOE_CHECK_PTR(shared_down);
+    }
+    MOE_CHECK_PTR(out);
+    size_t off[kLatTotal + 1];
+    latent_layout(shape, off);
+    st = check_ws(ws, ws_bytes, off[kLatTotal]);
+    if (st != MOE_OK) return st;
+    char* base = static_cast<char*>(ws);
+    auto at = [&](int slot) { return static_cast<void*>(base + off[slot]); };
+    float* logits = static_cast<float*>(at(MOE_LAT_LOGITS));
+    int32_t* idx = static_cast<int32_t*>(at(MOE_LAT_TOPK_IDX));
+    float* w = static_cast<float*>(at(MOE_LAT_TOPK_W));
+    int32_t* offsets = static_cast<int32_t*>(at(MOE_LAT_EXPERT_OFFSETS));
+    int32_t* row_of = static_cast<int32_t*>(at(MOE_LAT_ROW_OF));
+    int32_t* row_src = static_cast<int32_t*>(at(MOE_LAT_ROW_SRC));
+    uint16_t* z = static_cast<uint16_t*>(at(MOE_LAT_Z));
+    uint16_t* h_act = static_cast<uint16_t*>(at(MOE_LAT_H));
+    float* y_rows = static_cast<float*>(at(MOE_LAT_Y));
+    uint16_t* r = static_cast<uint16_t*>(at(MOE_LAT_R));
+    uint16_t* sh_h = static_cast<uint16_t*>(at(MOE_LAT_SHARED_H));
+    float* sh_y = static_cast<float*>(at(MOE_LAT_SHARED_Y));
+    int32_t* count_ws = static_cast<int32_t*>(at(kLatPermuteWs));
+    char* maps = static_cast<char*>(at(kLatMaps));
+    int32_t* dense_off = reinterpret_cast<int32_t*>(maps);
+    int32_t* shared_off = reinterpret_cast<int32_t*>(maps + maps_shared_off(shape));
+    int32_t* shared_rows = reinterpret_cast<int32_t*>(maps + maps_shared_rows(shape));
+    uint16_t* router_parts = static_cast<uint16_t*>(at(kLatRouteWs));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t T = shape->T, n = shape->T * shape->k;
+    const int d = shape->d, l = shape->l, E = shape->E, k = shape->k, h = shape->h;
+    const int S = shape->n_shared, hs = shape->h_shared;
+    const moe_shape_t rs{T, l, E, k, h};
+    const FfnWs fw = ffn_carve(&rs, at(kLatFfnWs));
+    const FfnWs dw = ffn_carve_rows(T, 1, at(kLatDenseWs));
+    const FfnWs sw = ffn_carve_rows(T * S, latent_groups(shape), at(kLatSharedWs));
+
+#define MOE_TRY(call, what)                              \
+    do {                                                 \
+        hipError_t e_ = (call);                          \
+        if (e_ != hipSuccess) return hip_status(e_, what); \
+    } while (0)
+    MOE_TRY(moe::launch_latent_maps(T, S, dense_off, shared_off, shared_rows, s), "latent_maps launch");
+    // router on x, then the grouping by expert
+    MOE_TRY(moe::launch_router_gemm(x, w_router, router_bias, logits, T, d, E, router_parts, s), "router_gemm launch");
+    MOE_TRY(moe::launch_topk_softmax(logits, T, E, k, idx, w, s), "topk_softmax launch");
+    MOE_TRY(moe::launch_permute(nullptr, idx, T, l, E, k, offsets, row_of, row_src, nullptr, count_ws, s),
+            "permute launch");
+    // z = x W_down_proj^T (bf16)
+    MOE_TRY(moe::launch_build_tiles(dense_off, T, 1, dw.tiles, dw.tile_start, s), "build_tiles launch");
+    MOE_TRY(moe::launch_dense(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s),
+            "down projection launch");
+    // routed experts on z (rows gathered through row_src), then u and RMSNorm(u)
+    MOE_TRY(moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s), "build_tiles launch");
+    MOE_TRY(moe::launch_gate_up(z, row_src, T, fw.tiles, fw.tile_start, n, l, E, h, w_gate, w_up, h_act, s),
+            "gate_up launch");
+    MOE_TRY(moe::launch_down(h_act, fw.tiles, fw.tile_start, n, l, E, h, w_down, y_rows, s), "down launch");
+    MOE_TRY(moe::launch_combine_rmsnorm(y_rows, row_of, w, T, l, k, n, rms_gain, rms_eps, nullptr, r, s),
+            "combine_rmsnorm launch");
+    // out = RMSNorm(u) W_up_proj^T (float32) ...
+    MOE_TRY(moe::launch_dense(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s),
+            "up projection launch");
+    if (S > 0) {  // ... + the shared experts on x
+        MOE_TRY(moe::launch_build_tiles(shared_off, T * S, S, sw.tiles, sw.tile_start, s), "build_tiles launch");
+        MOE_TRY(moe::launch_gate_up(x, shared_rows, T, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_gate,
+                                    shared_up, sh_h, s), "shared gate_up launch");
+        MOE_TRY(moe::launch_down(sh_h, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_down, sh_y, s),
+                "shared down launch");
+        MOE_TRY(moe::launch_add_shared(out, sh_y, T, d, S, s), "add_shared launch");
+    }
+#undef MOE_TRY
+    return ok();
 }
 
 }  // extern "C"

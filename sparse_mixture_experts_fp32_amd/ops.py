@@ -283,3 +283,85 @@ def moe_qb_update(hist, k: int, lo: float, width: float, bias_in, out=None):
         _lib.check(_lib.lib.moe_qb_update(ctypes.byref(s), _ptr(hist), lo, width, n_bins, _ptr(bias_in),
                                           _ptr(bias_out), _stream(dev)))
     return bias_out
+
+
+# ------------------------------------------------------------------ LatentMoE
+
+def moe_combine_rmsnorm(y_rows, row_of, topk_w, gain, eps: float, want_u: bool = False):
+    """r [T, l] bf16 = RMSNorm(u) with gain, u = sum_j topk_w[t, j] y_rows[row_of[t, j]]
+    (and u [T, l] f32 when want_u)."""
+    _need(y_rows, "y_rows", "f32")
+    dev = y_rows.device
+    n, l = y_rows.shape
+    T, k = row_of.shape
+    if n != T * k:
+        raise ValueError(f"y_rows has {n} rows, expected T*k = {T * k}")
+    _need(row_of, "row_of", "i32", (T, k), dev)
+    _need(topk_w, "topk_w", "f32", (T, k), dev)
+    _need(gain, "gain", "f32", (l,), dev)
+    s = _lib.shape(T, l, max(k, 1), k, 128)
+    r = torch.empty((T, l), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((T, l), dtype=torch.float32, device=dev) if want_u else None
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_combine_rmsnorm(ctypes.byref(s), _ptr(y_rows), _ptr(row_of), _ptr(topk_w), _ptr(gain),
+                                                eps, _ptr(u), _ptr(r), _stream(dev)))
+    return (r, u) if want_u else r
+
+
+class LatentMoEForward:
+    """moe_latent_forward with a reusable workspace (allocated once per shape)."""
+
+    def __init__(self, T: int, d: int, l: int, E: int, k: int, h: int, n_shared: int, h_shared: int, device):
+        self.shape = _lib.latent_shape(T, d, l, E, k, h, n_shared, h_shared)
+        self.T, self.d, self.l, self.E, self.k, self.h = T, d, l, E, k, h
+        self.S, self.hs = n_shared, h_shared
+        self.device = torch.device(device)
+        n = _lib.latent_workspace_bytes(self.shape)
+        self.ws = torch.empty(max(n, 1), dtype=torch.uint8, device=self.device)
+
+    def __call__(self, x, w_router, router_bias, w_proj_down, w_gate, w_up, w_down, rms_gain, rms_eps, w_proj_up,
+                 shared_gate=None, shared_up=None, shared_down=None, out=None):
+        T, d, l, E, k, h, S, hs, dev = self.T, self.d, self.l, self.E, self.k, self.h, self.S, self.hs, self.device
+        _need(x, "x", "bf16", (T, d), dev)
+        _need(w_router, "w_router", "f32", (E, d), dev)
+        if router_bias is not None:
+            _need(router_bias, "router_bias", "f32", (E,), dev)
+        _need(w_proj_down, "w_proj_down", "bf16", (l, d), dev)
+        _need(w_gate, "w_gate", "bf16", (E, h, l), dev)
+        _need(w_up, "w_up", "bf16", (E, h, l), dev)
+        _need(w_down, "w_down", "bf16", (E, l, h), dev)
+        _need(rms_gain, "rms_gain", "f32", (l,), dev)
+        _need(w_proj_up, "w_proj_up", "bf16", (d, l), dev)
+        if S > 0:
+            _need(shared_gate, "shared_gate", "bf16", (S, hs, d), dev)
+            _need(shared_up, "shared_up", "bf16", (S, hs, d), dev)
+            _need(shared_down, "shared_down", "bf16", (S, d, hs), dev)
+        if out is None:
+            out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        _need(out, "out", "f32", (T, d), dev)
+        with torch.cuda.device(dev):
+            _lib.check(_lib.lib.moe_latent_forward(
+                ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_proj_down),
+                _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(rms_gain), rms_eps, _ptr(w_proj_up),
+                _ptr(shared_gate if S > 0 else None), _ptr(shared_up if S > 0 else None),
+                _ptr(shared_down if S > 0 else None), _ptr(out), _ptr(self.ws), self.ws.numel(), _stream(dev)))
+        return out
+
+    def intermediate(self, name: str) -> torch.Tensor:
+        """A view of one intermediate that the last call left in the workspace."""
+        T, d, l, E, k, h, S, hs = self.T, self.d, self.l, self.E, self.k, self.h, self.S, self.hs
+        spec = {
+            "logits": (torch.float32, (T, E)), "topk_idx": (torch.int32, (T, k)),
+            "topk_w": (torch.float32, (T, k)), "expert_offsets": (torch.int32, (E + 1,)),
+            "row_of": (torch.int32, (T, k)), "row_src": (torch.int32, (T * k,)),
+            "z": (torch.bfloat16, (T, l)), "h_act": (torch.bfloat16, (T * k, h)),
+            "y_rows": (torch.float32, (T * k, l)), "r": (torch.bfloat16, (T, l)),
+            "shared_h": (torch.bfloat16, (S * T, hs)), "shared_y": (torch.float32, (S * T, d)),
+        }
+        dtype, shp = spec[name]
+        off = _lib.latent_ws_offset(self.shape, _lib.LAT_SLOTS.index(name))
+        n = 1
+        for v in shp:
+            n *= v
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype).view(shp)

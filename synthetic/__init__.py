@@ -11,3 +11,10 @@ from .moe_inputs import (  # noqa: F401
     make_inputs,
     scaled_config,
 )
+from .latent_inputs import (  # noqa: F401
+    LATENT_CONFIGS,
+    LatentConfig,
+    LatentInputs,
+    make_latent_inputs,
+    scaled_latent,
+)

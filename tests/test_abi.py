@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
               "moe_workspace_bytes", "moe_status_str", "moe_last_error", "moe_aux_loss",
-              "moe_qb_route", "moe_qb_histogram", "moe_qb_update"]:
+              "moe_qb_route", "moe_qb_histogram", "moe_qb_update", "moe_latent_forward",
+              "moe_latent_workspace_bytes", "moe_latent_ws_offset", "moe_combine_rmsnorm"]:
         assert n in names
 
 
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 4
+    assert L.moe_abi_version() == lib.ABI_VERSION == 5
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -183,3 +184,52 @@ def test_balance_calls_reject_bad_arguments(lib):
     s0 = _shape(lib, T=0)
     assert L.moe_aux_loss(ctypes.byref(s0), None, None, None, None, 0, None) == 0
     assert L.moe_qb_route(ctypes.byref(s0), None, None, None, None, None, None) == 0
+
+
+def test_latent_shape_checks_and_layout(lib):
+    L = lib.lib
+    a = ctypes.c_void_p(4096)
+    f = ctypes.c_float
+    good = dict(T=64, d=256, l=128, E=8, k=2, h=256, n_shared=2, h_shared=128)
+
+    def ls(**kw):
+        p = dict(good)
+        p.update(kw)
+        return lib.latent_shape(*(p[c] for c in ("T", "d", "l", "E", "k", "h", "n_shared", "h_shared")))
+
+    for bad, status in [(dict(l=96), 1), (dict(d=100), 1), (dict(n_shared=9), 1), (dict(n_shared=-1), 1),
+                        (dict(h_shared=0), 1), (dict(l=8192 + 128), 2), (dict(k=9), 1), (dict(T=-1), 1)]:
+        s = ls(**bad)
+        assert L.moe_latent_workspace_bytes(ctypes.byref(s)) == 0
+        assert L.moe_latent_forward(ctypes.byref(s), a, a, None, a, a, a, a, a, f(1e-6), a, a, a, a, a, a,
+                                    1 << 40, None) == status, (bad, L.moe_last_error())
+    s = ls()
+    need = lib.latent_workspace_bytes(s)
+    args = [a, a, None, a, a, a, a, a, f(1e-6), a, a, a, a, a]
+    assert L.moe_latent_forward(ctypes.byref(s), *args, a, need - 1, None) == 3
+    assert L.moe_latent_forward(ctypes.byref(s), *args[:8], f(-1.0), *args[9:], a, need, None) == 1
+    assert L.moe_latent_forward(ctypes.byref(s), *args[:10], None, *args[11:], a, need, None) == 1
+    s0 = ls(n_shared=0, h_shared=0)
+    args0 = [a, a, None, a, a, a, a, a, f(1e-6), a, None, None, None, a]
+    assert L.moe_latent_forward(ctypes.byref(s0), *args0, a, 1, None) == 3  # shared may be NULL; ws too small
+    # every slot inside the workspace, aligned, in order, sized as documented
+    for cfg in [good, dict(good, n_shared=0, h_shared=0),
+                dict(T=16384, d=7168, l=3584, E=896, k=16, h=1024, n_shared=2, h_shared=2048)]:
+        s = ls(**cfg)
+        total = lib.latent_workspace_bytes(s)
+        T, d, l, E, k, h, S, hs = (cfg[c] for c in ("T", "d", "l", "E", "k", "h", "n_shared", "h_shared"))
+        sizes = [4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k, 2 * T * l, 2 * T * k * h,
+                 4 * T * k * l, 2 * T * l, 2 * S * T * hs, 4 * S * T * d]
+        assert len(sizes) == len(lib.LAT_SLOTS)
+        offs = [lib.latent_ws_offset(s, i) for i in range(len(sizes))]
+        for i in range(len(sizes)):
+            assert offs[i] % 256 == 0 and offs[i] + sizes[i] <= total
+            if i + 1 < len(sizes):
+                assert offs[i] + sizes[i] <= offs[i + 1]
+    # combine_rmsnorm: width limit and eps
+    s = _shape(lib, d=8192 + 128)
+    assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, a, f(1e-6), None, a, None) == 2
+    s = _shape(lib)
+    assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, a, f(float("nan")), None, a, None) == 1
+    assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, None, f(1e-6), None, a, None) == 1
+    assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, a, f(1e-6), ctypes.c_void_p(4100), a, None) == 1
