@@ -66,10 +66,13 @@ E4M3 = dict(bits=8, table=_code_table(4, 3, 7, nan_codes=(0x7F,)), emax=8)
 
 
 def element_value(codes, fmt) -> np.ndarray:
-    """Value of each element code (sign bit on top)."""
+    """Value of each element code (sign bit on top), looked up in the format's table."""
     c = np.asarray(codes, dtype=np.int64)
     sign_bit = 1 << (fmt["bits"] - 1)
-    mag = np.vectorize(lambda x: fmt["table"][int(x) & (sign_bit - 1)], otypes=[np.float64])(c)
+    lut = np.full(sign_bit, np.nan)
+    for code, v in fmt["table"].items():
+        lut[code] = v
+    mag = lut[c & (sign_bit - 1)]
     return np.where(c & sign_bit, -mag, mag)
 
 
