@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -70,7 +70,8 @@ typedef enum moe_call {
     MOE_CALL_EXPERT_FFN = 1,
     MOE_CALL_FORWARD = 2,
     MOE_CALL_ROUTE = 3,
-    MOE_CALL_AUX_LOSS = 4
+    MOE_CALL_AUX_LOSS = 4,
+    MOE_CALL_MX_FORWARD = 5
 } moe_call_t;
 
 /* Intermediates that moe_forward keeps in its workspace (see moe_forward_ws_offset). */
@@ -365,6 +366,86 @@ int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const
 int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of,
                         const float* topk_w, const float* gain, float eps, float* u_out, uint16_t* r_out,
                         void* stream);
+
+/*
+ * --------------------------------------------------------------- MX experts
+ * The serving variant of the routed layer ("Kimi K3: Open Frontier
+ * Intelligence", section "Systems Optimization, Load Balancing, and
+ * Post-Training Alignment"): MoE weights in MXFP4, activations in MXFP8. The
+ * formats are the OCP Microscaling v1.0 ones: blocks of 32 consecutive elements
+ * along K (the contraction dimension) share an E8M0 scale byte (2^(byte - 127));
+ * elements are E2M1 (MXFP4) or E4M3 (MXFP8). Conversion of a block:
+ * s = floor(log2 max|v|) - emax (emax 2 for E2M1, 8 for E4M3; s = -127 for an
+ * all-zero block, clamped to [-127, 127]); each element is v / 2^s rounded to
+ * the nearest element value, ties to the even code, clamped to the largest
+ * value (6 or 448); a value that rounds to zero keeps its sign.
+ * The MX calls need d and h to be multiples of 512.
+ *
+ * Layouts:
+ *  - MXFP4 weights of G matrices [N, K]: codes [G, N, K/2] bytes, element 2i of
+ *    a row in the low nibble of byte i; scales [G, N, K/32] bytes in the
+ *    matrix-core order: the scale of block kb of row n sits at byte
+ *    n*(K/32) + (kb/16)*16 + (kb%4)*4 + (kb/4)%4 of its matrix.
+ *  - MXFP8 rows [R, K]: codes [R, K] bytes; scales [R, K/32] bytes in row order.
+ */
+
+/* Quantise bf16 weights w [groups, N, K] to MXFP4 (K a multiple of 512). */
+int moe_mx_quantize_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint8_t* q,
+                            uint8_t* scales, void* stream);
+
+/* Quantise rows [rows, K] (bf16, or float32 when in_is_f32) to MXFP8 (K a multiple of 32). */
+int moe_mx_quantize_rows(int64_t rows, int32_t K, const void* in, int32_t in_is_f32, uint8_t* q,
+                         uint8_t* scales, void* stream);
+
+/*
+ * moe_mx_expert_ffn -- every expert's SwiGLU FFN on its rows with MX operands.
+ *  a_q, a_s   MXFP8 rows: [T * k, d] and [T * k, d/32] when a_rows is NULL, else
+ *             the token rows [T, d] / [T, d/32] read through a_rows (= row_src)
+ *  expert_offsets [E + 1] int32 (as moe_permute writes them)
+ *  wg_*, wu_* MXFP4 gate and up weights of [E, h, d]; wd_* MXFP4 down weights of [E, d, h]
+ *  h_act  [T * k, h] float32 out: silu(gate) * up, float32 accumulation of the exact products
+ *  h_q, h_s [T * k, h], [T * k, h/32] out: h_act quantised to MXFP8 (codes decided on h_act)
+ *  y_rows [T * k, d] float32 out
+ *  ws, ws_bytes  workspace of at least moe_workspace_bytes(shape, MOE_CALL_EXPERT_FFN)
+ */
+int moe_mx_expert_ffn(const moe_shape_t* shape, const uint8_t* a_q, const uint8_t* a_s,
+                      const int32_t* a_rows, const int32_t* expert_offsets, const uint8_t* wg_q,
+                      const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, const uint8_t* wd_q,
+                      const uint8_t* wd_s, float* h_act, uint8_t* h_q, uint8_t* h_s, float* y_rows,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Intermediates moe_mx_forward leaves in its workspace (moe_mx_forward_ws_offset). */
+typedef enum moe_mx_slot {
+    MOE_MX_LOGITS = 0,         /* [T, E] float32 */
+    MOE_MX_TOPK_IDX = 1,       /* [T, k] int32 */
+    MOE_MX_TOPK_W = 2,         /* [T, k] float32 */
+    MOE_MX_EXPERT_OFFSETS = 3, /* [E + 1] int32 */
+    MOE_MX_ROW_OF = 4,         /* [T, k] int32 */
+    MOE_MX_ROW_SRC = 5,        /* [T * k] int32 */
+    MOE_MX_X_Q = 6,            /* [T, d] MXFP8 codes of x */
+    MOE_MX_X_S = 7,            /* [T, d/32] their scales */
+    MOE_MX_H = 8,              /* [T * k, h] float32 */
+    MOE_MX_H_Q = 9,            /* [T * k, h] MXFP8 codes of H */
+    MOE_MX_H_S = 10,           /* [T * k, h/32] their scales */
+    MOE_MX_Y = 11,             /* [T * k, d] float32 */
+    MOE_MX_NUM_SLOTS = 12
+} moe_mx_slot_t;
+
+int moe_mx_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset);
+
+/*
+ * moe_mx_forward -- the routed layer with MXFP4 experts: moe_route, moe_permute
+ * (no gather), x quantised to MXFP8, moe_mx_expert_ffn reading x's codes through
+ * row_src, moe_combine.
+ *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL;
+ *  wg_*, wu_*, wd_* MXFP4 expert weights (moe_mx_quantize_weights layouts)
+ *  out [T, d] float32 (written)
+ *  ws, ws_bytes  workspace of at least moe_workspace_bytes(shape, MOE_CALL_MX_FORWARD)
+ */
+int moe_mx_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
+                   const float* router_bias, const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q,
+                   const uint8_t* wu_s, const uint8_t* wd_q, const uint8_t* wd_s, float* out, void* ws,
+                   size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,11 +23,14 @@ MOE_CALL_EXPERT_FFN = 1
 MOE_CALL_FORWARD = 2
 MOE_CALL_ROUTE = 3
 MOE_CALL_AUX_LOSS = 4
+MOE_CALL_MX_FORWARD = 5
 
+MX_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "x_q", "x_s", "h_act", "h_q",
+            "h_s", "y_rows"]
 LAT_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "z", "h_act", "y_rows", "r",
              "shared_h", "shared_y"]
 FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class MoeShape(ctypes.Structure):
@@ -77,6 +80,11 @@ def _load():
         "moe_latent_forward": (ctypes.c_int, [LS, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
                                               ctypes.c_size_t, P]),
         "moe_combine_rmsnorm": (ctypes.c_int, [S, P, P, P, P, ctypes.c_float, P, P, P]),
+        "moe_mx_quantize_weights": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
+        "moe_mx_quantize_rows": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32, P, P, P]),
+        "moe_mx_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_mx_forward_ws_offset": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+        "moe_mx_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -129,4 +137,10 @@ def latent_workspace_bytes(s: MoeLatentShape) -> int:
 def latent_ws_offset(s: MoeLatentShape, slot: int) -> int:
     off = ctypes.c_size_t(0)
     check(lib.moe_latent_ws_offset(ctypes.byref(s), slot, ctypes.byref(off)))
+    return off.value
+
+
+def mx_forward_ws_offset(s: MoeShape, slot: int) -> int:
+    off = ctypes.c_size_t(0)
+    check(lib.moe_mx_forward_ws_offset(ctypes.byref(s), slot, ctypes.byref(off)))
     return off.value

@@ -56,4 +56,12 @@ hipError_t launch_latent_maps(int64_t T, int S, int32_t* dense_off, int32_t* sha
                               hipStream_t stream);
 hipError_t launch_add_shared(float* out, const float* ys, int64_t T, int d, int S, hipStream_t stream);
 
+int mx_tile_rows();
+hipError_t launch_mx_quantize(const void* in, bool in_f32, int64_t rows, int K, bool fp4, uint8_t* q,
+                              uint8_t* scales, hipStream_t stream);
+hipError_t launch_mx_ffn_pass(bool gated, const uint8_t* a, const uint8_t* a_scales, const int32_t* a_rows,
+                              int64_t a_nrows, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int E,
+                              const uint8_t* w0q, const uint8_t* w0s, const uint8_t* w1q, const uint8_t* w1s, int N,
+                              int K, float* c, hipStream_t stream);
+
 }  // namespace moe

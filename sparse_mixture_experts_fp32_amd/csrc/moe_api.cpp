@@ -213,6 +213,36 @@ void forward_layout(const moe_shape_t* s, size_t off[kFwdTotal + 1]) {
     off[kFwdTotal] = at;
 }
 
+int check_mx_shape(const moe_shape_t* s) {
+    int st = check_shape(s);
+    if (st != MOE_OK) return st;
+    // the MX passes walk the same m-tile list as the bf16 passes
+    if (moe::mx_tile_rows() != moe::ffn_tile_rows())
+        return fail(MOE_ERR_UNSUPPORTED, "MX and bf16 m-tile heights differ (%d vs %d)", moe::mx_tile_rows(),
+                    moe::ffn_tile_rows());
+    if (s->d % 512 != 0 || s->h % 512 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "the MX path needs d and h to be multiples of 512 (d = %d, h = %d)", s->d,
+                    s->h);
+    return MOE_OK;
+}
+
+// MX forward slots, then the permute scratch, the tile list and the router parts.
+constexpr int kMxPermuteWs = MOE_MX_NUM_SLOTS, kMxFfnWs = MOE_MX_NUM_SLOTS + 1, kMxRouteWs = MOE_MX_NUM_SLOTS + 2,
+              kMxTotal = MOE_MX_NUM_SLOTS + 3;
+
+void mx_layout(const moe_shape_t* s, size_t off[kMxTotal + 1]) {
+    const size_t T = static_cast<size_t>(s->T), E = s->E, k = s->k, d = s->d, h = s->h;
+    const size_t sizes[kMxTotal] = {4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k,
+                                    T * d, T * d / 32, 4 * T * k * h, T * k * h, T * k * h / 32, 4 * T * k * d,
+                                    permute_ws(s), ffn_ws(s), route_ws(s)};
+    size_t at = 0;
+    for (int i = 0; i < kMxTotal; ++i) {
+        off[i] = at;
+        at += align_up(sizes[i]);
+    }
+    off[kMxTotal] = at;
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +269,13 @@ size_t moe_workspace_bytes(const moe_shape_t* shape, int call) {
         case MOE_CALL_EXPERT_FFN: ok(); return ffn_ws(shape);
         case MOE_CALL_ROUTE: ok(); return route_ws(shape);
         case MOE_CALL_AUX_LOSS: ok(); return aux_ws(shape);
+        case MOE_CALL_MX_FORWARD: {
+            if (check_mx_shape(shape) != MOE_OK) return 0;
+            size_t off[kMxTotal + 1];
+            mx_layout(shape, off);
+            ok();
+            return off[kMxTotal];
+        }
         case MOE_CALL_FORWARD: {
             size_t off[kFwdTotal + 1];
             forward_layout(shape, off);
@@ -649,6 +686,150 @@ int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const
     }
 #undef MOE_TRY
     return ok();
+}
+
+int moe_mx_quantize_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint8_t* q, uint8_t* scales,
+                            void* stream) {
+    if (groups < 0 || N < 0 || K < 512 || K % 512 != 0 || K > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "bad weight shape (groups %lld, N %d, K %d; K a multiple of 512)",
+                    static_cast<long long>(groups), N, K);
+    if (groups * N * static_cast<int64_t>(K / 32) >= (int64_t(1) << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "weights too large");
+    if (groups == 0 || N == 0) return ok();
+    MOE_CHECK_PTR(w);
+    MOE_CHECK_PTR(q);
+    MOE_CHECK_PTR(scales);
+    hipError_t err = moe::launch_mx_quantize(w, false, groups * N, K, true, q, scales,
+                                             static_cast<hipStream_t>(stream));
+    return hip_status(err, "mx_quantize launch");
+}
+
+int moe_mx_quantize_rows(int64_t rows, int32_t K, const void* in, int32_t in_is_f32, uint8_t* q, uint8_t* scales,
+                         void* stream) {
+    if (rows < 0 || K < 32 || K % 32 != 0 || K > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "bad row shape (rows %lld, K %d; K a multiple of 32)",
+                    static_cast<long long>(rows), K);
+    if (rows == 0) return ok();
+    MOE_CHECK_PTR(in);
+    MOE_CHECK_PTR(q);
+    if (scales == nullptr) return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
+    hipError_t err = moe::launch_mx_quantize(in, in_is_f32 != 0, rows, K, false, q, scales,
+                                             static_cast<hipStream_t>(stream));
+    return hip_status(err, "mx_quantize launch");
+}
+
+int moe_mx_expert_ffn(const moe_shape_t* shape, const uint8_t* a_q, const uint8_t* a_s, const int32_t* a_rows,
+                      const int32_t* expert_offsets, const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q,
+                      const uint8_t* wu_s, const uint8_t* wd_q, const uint8_t* wd_s, float* h_act, uint8_t* h_q,
+                      uint8_t* h_s, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_mx_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(a_q);
+    MOE_CHECK_PTR(a_s);
+    if (a_rows != nullptr && !aligned16(a_rows)) return fail(MOE_ERR_INVALID_ARG, "a_rows is not 16-byte aligned");
+    MOE_CHECK_PTR(expert_offsets);
+    MOE_CHECK_PTR(wg_q);
+    MOE_CHECK_PTR(wg_s);
+    MOE_CHECK_PTR(wu_q);
+    MOE_CHECK_PTR(wu_s);
+    MOE_CHECK_PTR(wd_q);
+    MOE_CHECK_PTR(wd_s);
+    MOE_CHECK_PTR(h_act);
+    MOE_CHECK_PTR(h_q);
+    MOE_CHECK_PTR(h_s);
+    MOE_CHECK_PTR(y_rows);
+    st = check_ws(ws, ws_bytes, ffn_ws(shape));
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = shape->T * shape->k;
+    const int d = shape->d, E = shape->E, h = shape->h;
+    const FfnWs fw = ffn_carve(shape, ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, E, fw.tiles, fw.tile_start, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_mx_ffn_pass(true, a_q, a_s, a_rows, a_rows ? shape->T : n, fw.tiles, fw.tile_start, n, E,
+                                  wg_q, wg_s, wu_q, wu_s, h, d, h_act, s);
+    if (err != hipSuccess) return hip_status(err, "mx gate_up launch");
+    err = moe::launch_mx_quantize(h_act, true, n, h, false, h_q, h_s, s);
+    if (err != hipSuccess) return hip_status(err, "mx_quantize launch");
+    err = moe::launch_mx_ffn_pass(false, h_q, h_s, nullptr, n, fw.tiles, fw.tile_start, n, E, wd_q, wd_s, nullptr,
+                                  nullptr, d, h, y_rows, s);
+    return hip_status(err, "mx down launch");
+}
+
+int moe_mx_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset) {
+    int st = check_mx_shape(shape);
+    if (st != MOE_OK) return st;
+    if (slot < 0 || slot >= MOE_MX_NUM_SLOTS) return fail(MOE_ERR_INVALID_ARG, "unknown slot %d", slot);
+    if (offset == nullptr) return fail(MOE_ERR_INVALID_ARG, "offset is NULL");
+    size_t off[kMxTotal + 1];
+    mx_layout(shape, off);
+    *offset = off[slot];
+    return ok();
+}
+
+int moe_mx_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+                   const uint8_t* wg_q, const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s,
+                   const uint8_t* wd_q, const uint8_t* wd_s, float* out, void* ws, size_t ws_bytes, void* stream) {
+    int st = check_mx_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(x);
+    MOE_CHECK_PTR(w_router);
+    if (router_bias != nullptr && !aligned16(router_bias))
+        return fail(MOE_ERR_INVALID_ARG, "router_bias is not 16-byte aligned");
+    MOE_CHECK_PTR(wg_q);
+    MOE_CHECK_PTR(wg_s);
+    MOE_CHECK_PTR(wu_q);
+    MOE_CHECK_PTR(wu_s);
+    MOE_CHECK_PTR(wd_q);
+    MOE_CHECK_PTR(wd_s);
+    MOE_CHECK_PTR(out);
+    size_t off[kMxTotal + 1];
+    mx_layout(shape, off);
+    st = check_ws(ws, ws_bytes, off[kMxTotal]);
+    if (st != MOE_OK) return st;
+    char* base = static_cast<char*>(ws);
+    auto at = [&](int slot) { return static_cast<void*>(base + off[slot]); };
+    float* logits = static_cast<float*>(at(MOE_MX_LOGITS));
+    int32_t* idx = static_cast<int32_t*>(at(MOE_MX_TOPK_IDX));
+    float* w = static_cast<float*>(at(MOE_MX_TOPK_W));
+    int32_t* offsets = static_cast<int32_t*>(at(MOE_MX_EXPERT_OFFSETS));
+    int32_t* row_of = static_cast<int32_t*>(at(MOE_MX_ROW_OF));
+    int32_t* row_src = static_cast<int32_t*>(at(MOE_MX_ROW_SRC));
+    uint8_t* x_q = static_cast<uint8_t*>(at(MOE_MX_X_Q));
+    uint8_t* x_s = static_cast<uint8_t*>(at(MOE_MX_X_S));
+    float* h_act = static_cast<float*>(at(MOE_MX_H));
+    uint8_t* h_q = static_cast<uint8_t*>(at(MOE_MX_H_Q));
+    uint8_t* h_s = static_cast<uint8_t*>(at(MOE_MX_H_S));
+    float* y_rows = static_cast<float*>(at(MOE_MX_Y));
+    int32_t* count_ws = static_cast<int32_t*>(at(kMxPermuteWs));
+    const FfnWs fw = ffn_carve(shape, at(kMxFfnWs));
+    uint16_t* router_parts = static_cast<uint16_t*>(at(kMxRouteWs));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t T = shape->T, n = shape->T * shape->k;
+    const int d = shape->d, E = shape->E, k = shape->k, h = shape->h;
+
+    hipError_t err = moe::launch_router_gemm(x, w_router, router_bias, logits, T, d, E, router_parts, s);
+    if (err != hipSuccess) return hip_status(err, "router_gemm launch");
+    err = moe::launch_topk_softmax(logits, T, E, k, idx, w, s);
+    if (err != hipSuccess) return hip_status(err, "topk_softmax launch");
+    err = moe::launch_permute(x, idx, T, d, E, k, offsets, row_of, row_src, nullptr, count_ws, s);
+    if (err != hipSuccess) return hip_status(err, "permute launch");
+    err = moe::launch_mx_quantize(x, false, T, d, false, x_q, x_s, s);
+    if (err != hipSuccess) return hip_status(err, "mx_quantize launch");
+    err = moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_mx_ffn_pass(true, x_q, x_s, row_src, T, fw.tiles, fw.tile_start, n, E, wg_q, wg_s, wu_q, wu_s,
+                                  h, d, h_act, s);
+    if (err != hipSuccess) return hip_status(err, "mx gate_up launch");
+    err = moe::launch_mx_quantize(h_act, true, n, h, false, h_q, h_s, s);
+    if (err != hipSuccess) return hip_status(err, "mx_quantize launch");
+    err = moe::launch_mx_ffn_pass(false, h_q, h_s, nullptr, n, fw.tiles, fw.tile_start, n, E, wd_q, wd_s, nullptr,
+                                  nullptr, d, h, y_rows, s);
+    if (err != hipSuccess) return hip_status(err, "mx down launch");
+    err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
+    return hip_status(err, "combine launch");
 }
 
 }  // extern "C"

@@ -365,3 +365,120 @@ class LatentMoEForward:
             n *= v
         nbytes = n * torch.tensor([], dtype=dtype).element_size()
         return self.ws[off:off + nbytes].view(dtype).view(shp)
+
+
+# ------------------------------------------------------------------ MX experts
+
+_U8 = torch.uint8
+
+
+def moe_mx_quantize_weights(w):
+    """MXFP4 codes [G, N, K/2] u8 (two per byte, low nibble first) and E8M0 scales [G, N, K/32] u8
+    (matrix-core order) of bf16 weights w [G, N, K]."""
+    _need(w, "w", "bf16")
+    dev = w.device
+    G, N, K = w.shape
+    q = torch.empty((G, N, K // 2), dtype=_U8, device=dev)
+    sc = torch.empty((G, N, K // 32), dtype=_U8, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_mx_quantize_weights(G, N, K, _ptr(w), _ptr(q), _ptr(sc), _stream(dev)))
+    return q, sc
+
+
+def moe_mx_quantize_rows(x):
+    """MXFP8 codes [R, K] u8 and E8M0 scales [R, K/32] u8 (row order) of rows x [R, K] (bf16 or f32)."""
+    if not isinstance(x, torch.Tensor) or x.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("x must be a bf16 or float32 tensor")
+    _need(x, "x", "bf16" if x.dtype == torch.bfloat16 else "f32")
+    dev = x.device
+    R, K = x.shape
+    q = torch.empty((R, K), dtype=_U8, device=dev)
+    sc = torch.empty((R, K // 32), dtype=_U8, device=dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_mx_quantize_rows(R, K, _ptr(x), int(x.dtype == torch.float32), _ptr(q), _ptr(sc),
+                                                 _stream(dev)))
+    return q, sc
+
+
+def _need_u8(t, name, shape, dev):
+    if not isinstance(t, torch.Tensor) or t.dtype != _U8 or t.device != dev or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous uint8 tensor on {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def moe_mx_expert_ffn(a_q, a_s, expert_offsets, gate, up, down, T: int, k: int, h: int, a_rows=None):
+    """MX expert FFN. gate, up, down are (codes, scales) pairs from moe_mx_quantize_weights of
+    [E, h, d], [E, h, d], [E, d, h]; a_q/a_s are MXFP8 rows ([T*k, d], or [T, d] read through a_rows).
+    Returns h_act [T*k, h] f32, h_q [T*k, h] u8, h_s [T*k, h/32] u8, y_rows [T*k, d] f32."""
+    dev = a_q.device
+    n = T * k
+    d = a_q.shape[1]
+    E = expert_offsets.shape[0] - 1
+    _need_u8(a_q, "a_q", (n if a_rows is None else T, d), dev)
+    _need_u8(a_s, "a_s", (n if a_rows is None else T, d // 32), dev)
+    if a_rows is not None:
+        _need(a_rows, "a_rows", "i32", (n,), dev)
+    _need(expert_offsets, "expert_offsets", "i32", (E + 1,), dev)
+    for name, (q, sc), (N, K) in (("gate", gate, (h, d)), ("up", up, (h, d)), ("down", down, (d, h))):
+        _need_u8(q, f"{name} codes", (E, N, K // 2), dev)
+        _need_u8(sc, f"{name} scales", (E, N, K // 32), dev)
+    s = _lib.shape(T, d, E, k, h)
+    h_act = torch.empty((n, h), dtype=torch.float32, device=dev)
+    h_q = torch.empty((n, h), dtype=_U8, device=dev)
+    h_s = torch.empty((n, h // 32), dtype=_U8, device=dev)
+    y = torch.empty((n, d), dtype=torch.float32, device=dev)
+    ws = workspace(s, _lib.MOE_CALL_EXPERT_FFN, dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_mx_expert_ffn(ctypes.byref(s), _ptr(a_q), _ptr(a_s), _ptr(a_rows),
+                                              _ptr(expert_offsets), _ptr(gate[0]), _ptr(gate[1]), _ptr(up[0]),
+                                              _ptr(up[1]), _ptr(down[0]), _ptr(down[1]), _ptr(h_act), _ptr(h_q),
+                                              _ptr(h_s), _ptr(y), _ptr(ws), ws.numel(), _stream(dev)))
+    return h_act, h_q, h_s, y
+
+
+class MXForward:
+    """moe_mx_forward with a reusable workspace; expert weights are (codes, scales) pairs."""
+
+    def __init__(self, T: int, d: int, E: int, k: int, h: int, device):
+        self.shape = _lib.shape(T, d, E, k, h)
+        self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
+        self.device = torch.device(device)
+        self.ws = workspace(self.shape, _lib.MOE_CALL_MX_FORWARD, self.device)
+
+    def __call__(self, x, w_router, router_bias, gate, up, down, out=None):
+        T, d, E, k, h, dev = self.T, self.d, self.E, self.k, self.h, self.device
+        _need(x, "x", "bf16", (T, d), dev)
+        _need(w_router, "w_router", "f32", (E, d), dev)
+        if router_bias is not None:
+            _need(router_bias, "router_bias", "f32", (E,), dev)
+        for name, (q, sc), (N, K) in (("gate", gate, (h, d)), ("up", up, (h, d)), ("down", down, (d, h))):
+            _need_u8(q, f"{name} codes", (E, N, K // 2), dev)
+            _need_u8(sc, f"{name} scales", (E, N, K // 32), dev)
+        if out is None:
+            out = torch.empty((T, d), dtype=torch.float32, device=dev)
+        _need(out, "out", "f32", (T, d), dev)
+        with torch.cuda.device(dev):
+            _lib.check(_lib.lib.moe_mx_forward(ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias),
+                                               _ptr(gate[0]), _ptr(gate[1]), _ptr(up[0]), _ptr(up[1]),
+                                               _ptr(down[0]), _ptr(down[1]), _ptr(out), _ptr(self.ws),
+                                               self.ws.numel(), _stream(dev)))
+        return out
+
+    def intermediate(self, name: str) -> torch.Tensor:
+        T, d, E, k, h = self.T, self.d, self.E, self.k, self.h
+        n = T * k
+        spec = {
+            "logits": (torch.float32, (T, E)), "topk_idx": (torch.int32, (T, k)),
+            "topk_w": (torch.float32, (T, k)), "expert_offsets": (torch.int32, (E + 1,)),
+            "row_of": (torch.int32, (T, k)), "row_src": (torch.int32, (n,)),
+            "x_q": (_U8, (T, d)), "x_s": (_U8, (T, d // 32)), "h_act": (torch.float32, (n, h)),
+            "h_q": (_U8, (n, h)), "h_s": (_U8, (n, h // 32)), "y_rows": (torch.float32, (n, d)),
+        }
+        dtype, shp = spec[name]
+        off = _lib.mx_forward_ws_offset(self.shape, _lib.MX_SLOTS.index(name))
+        cnt = 1
+        for v in shp:
+            cnt *= v
+        nbytes = cnt * torch.tensor([], dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype).view(shp)

@@ -37,7 +37,9 @@ def test_header_declares_the_boundary():
     for n in ["moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_forward",
               "moe_workspace_bytes", "moe_status_str", "moe_last_error", "moe_aux_loss",
               "moe_qb_route", "moe_qb_histogram", "moe_qb_update", "moe_latent_forward",
-              "moe_latent_workspace_bytes", "moe_latent_ws_offset", "moe_combine_rmsnorm"]:
+              "moe_latent_workspace_bytes", "moe_latent_ws_offset", "moe_combine_rmsnorm",
+              "moe_mx_quantize_weights", "moe_mx_quantize_rows", "moe_mx_expert_ffn", "moe_mx_forward",
+              "moe_mx_forward_ws_offset"]:
         assert n in names
 
 
@@ -52,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 5
+    assert L.moe_abi_version() == lib.ABI_VERSION == 6
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -233,3 +235,35 @@ def test_latent_shape_checks_and_layout(lib):
     assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, a, f(float("nan")), None, a, None) == 1
     assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, None, f(1e-6), None, a, None) == 1
     assert L.moe_combine_rmsnorm(ctypes.byref(s), a, a, a, a, f(1e-6), ctypes.c_void_p(4100), a, None) == 1
+
+
+def test_mx_calls_check_arguments(lib):
+    L = lib.lib
+    a = ctypes.c_void_p(4096)
+    # d and h must be multiples of 512 for the MX path
+    s = _shape(lib, d=256, h=512)
+    assert L.moe_mx_forward(ctypes.byref(s), a, a, None, a, a, a, a, a, a, a, a, 1 << 30, None) == 2
+    assert L.moe_workspace_bytes(ctypes.byref(s), lib.MOE_CALL_MX_FORWARD) == 0
+    s = _shape(lib, d=512, h=512)
+    need = lib.workspace_bytes(s, lib.MOE_CALL_MX_FORWARD)
+    assert need > 0 and need % 256 == 0
+    assert L.moe_mx_forward(ctypes.byref(s), a, a, None, a, a, a, a, a, a, a, a, need - 1, None) == 3
+    assert L.moe_mx_forward(ctypes.byref(s), a, a, None, a, None, a, a, a, a, a, a, need, None) == 1
+    assert L.moe_mx_expert_ffn(ctypes.byref(s), a, a, None, a, a, a, a, a, a, a, a, None, a, a, a, 1 << 20,
+                               None) == 1
+    assert L.moe_mx_quantize_weights(2, 16, 256, a, a, a, None) == 1       # K not a multiple of 512
+    assert L.moe_mx_quantize_weights(2, 16, 512, None, a, a, None) == 1
+    assert L.moe_mx_quantize_weights(0, 16, 512, None, None, None, None) == 0
+    assert L.moe_mx_quantize_rows(4, 48, a, 0, a, a, None) == 1             # K not a multiple of 32
+    assert L.moe_mx_quantize_rows(0, 64, None, 0, None, None, None) == 0
+    T, d, E, k, h = 64, 512, 8, 2, 512
+    sizes = [4 * T * E, 4 * T * k, 4 * T * k, 4 * (E + 1), 4 * T * k, 4 * T * k, T * d, T * d // 32,
+             4 * T * k * h, T * k * h, T * k * h // 32, 4 * T * k * d]
+    s = lib.shape(T, d, E, k, h)
+    total = lib.workspace_bytes(s, lib.MOE_CALL_MX_FORWARD)
+    assert len(sizes) == len(lib.MX_SLOTS)
+    offs = [lib.mx_forward_ws_offset(s, i) for i in range(len(sizes))]
+    for i in range(len(sizes)):
+        assert offs[i] % 256 == 0 and offs[i] + sizes[i] <= total
+        if i + 1 < len(sizes):
+            assert offs[i] + sizes[i] <= offs[i + 1]

@@ -1,0 +1,256 @@
+"""GPU parity of the MX-format expert path (MXFP4 weights, MXFP8 activations)
+against the CPU oracle, through the C ABI.
+
+  * codes and scales (weights, x rows, H rows): bit for bit. H's codes are
+    compared with the oracle's quantisation of the device's own float32 H, so
+    both sides decide on the same numbers;
+  * H = silu(G) U from exact products accumulated in float32: with A_G, A_U
+    the sums of |products| and gamma = K 2^-24,
+    |dH| <= 1.1 gamma A_G |U| + (|G| + 0.3) gamma A_U + 1e-6 |H|;
+  * Y rows: |dY| <= gamma_h * sum_k |h_k w_k| + 1e-30;
+  * out against the oracle's combine of the device's Y rows: (k + 1) 2^-23 sum_j |w_j y_j|;
+  * the layer end to end against the oracle's own MX layer (device logits):
+    max rel <= 2e-2, mean abs <= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as orc
+import oracle.mx as mx
+from synthetic import make_inputs, scaled_config
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_mixture_experts_fp32_amd  # noqa: F401  (fails loudly if libmoe.so is missing)
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def moe(dev):
+    import sparse_mixture_experts_fp32_amd as m
+    return m
+
+
+def unpack_fp4(q):
+    """[..., K/2] bytes -> [..., K] codes, element 2i in the low nibble of byte i."""
+    q = gu.host(q).numpy().astype(np.int64)
+    out = np.empty(q.shape[:-1] + (2 * q.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = q & 0xF
+    out[..., 1::2] = q >> 4
+    return out
+
+
+def unswizzle_scales(sc):
+    """Weight scales [..., K/32] from the matrix-core order to row order: block kb of a
+    row sits at byte (kb // 16) * 16 + (kb % 4) * 4 + (kb // 4) % 4 of that row."""
+    sc = gu.host(sc).numpy().astype(np.int64)
+    nb = sc.shape[-1]
+    kb = np.arange(nb)
+    pos = (kb // 16) * 16 + (kb % 4) * 4 + (kb // 4) % 4
+    return sc[..., pos]
+
+
+def _u8(t):
+    return gu.host(t).numpy().astype(np.int64)
+
+
+def _planted_weights(r, G, N, K):
+    w = (r.standard_normal((G, N, K)) / np.sqrt(K)).astype(np.float32)
+    w[0, 0, :32] = 0.0                                          # an all-zero block
+    w[0, 1, :32] = -0.0                                         # negative zeros
+    w[0, 2, :32] = np.array([6, 5, 2.5, 0.25, 0.75, 1.25, 1.75, 3.5] * 4) * 2.0 ** -7  # ties
+    w[0, 3, 32:64] = 7.9 * 2.0 ** -5                           # clamping from below 8
+    w[-1, -1, -32:] = r.standard_normal(32) * 1e-30             # tiny block
+    return torch.from_numpy(w).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("G,N,K", [(3, 48, 512), (1, 16, 1024), (2, 32, 2048)])
+def test_mx_quantize_weights_bitexact(dev, moe, G, N, K):
+    w = _planted_weights(np.random.default_rng(G * N + K), G, N, K)
+    q, sc = moe.moe_mx_quantize_weights(w.to(dev))
+    torch.cuda.synchronize()
+    codes_ref, s_ref = mx.quantize(gu.f64(w), mx.E2M1)
+    codes = unpack_fp4(q)
+    bad = np.argwhere(codes != codes_ref)
+    assert bad.size == 0, f"E2M1 codes differ at {bad[:5].tolist()}"
+    assert np.array_equal(unswizzle_scales(sc), s_ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("R,K", [(37, 64), (5, 7168), (130, 512)])
+def test_mx_quantize_rows_bitexact(dev, moe, dtype, R, K):
+    r = np.random.default_rng(R + K)
+    x = (r.standard_normal((R, K)) * np.exp(r.uniform(-6, 6, size=(R, 1)))).astype(np.float32)
+    x[0, :32] = 0.0
+    x[0, 32:64] = np.array([448, 1.0625, 1.1875, 248, 3 * 2.0 ** -10, 2.0 ** -10, -0.0, 460] * 4) * 2.0 ** 3
+    xt = torch.from_numpy(x).to(dtype)
+    q, sc = moe.moe_mx_quantize_rows(xt.to(dev))
+    torch.cuda.synchronize()
+    codes_ref, s_ref = mx.quantize(gu.f64(xt), mx.E4M3)
+    bad = np.argwhere(_u8(q) != codes_ref)
+    assert bad.size == 0, f"E4M3 codes differ at {bad[:5].tolist()}"
+    assert np.array_equal(_u8(sc), s_ref)
+
+
+# ------------------------------------------------------------- the layer
+
+def _mx_weights(moe, inp, dev):
+    return (moe.moe_mx_quantize_weights(inp.w_gate), moe.moe_mx_quantize_weights(inp.w_up),
+            moe.moe_mx_quantize_weights(inp.w_down))
+
+
+def _deq_w(pair, e):
+    q, sc = pair
+    return mx.dequantize(unpack_fp4(q[e]), unswizzle_scales(sc[e]), mx.E2M1)
+
+
+def _check_h(h_dev, X, Wg, Wu):
+    d = X.shape[1]
+    gamma = d * 2.0 ** -24
+    G, U = X @ Wg.T, X @ Wu.T
+    AG, AU = np.abs(X) @ np.abs(Wg).T, np.abs(X) @ np.abs(Wu).T
+    H = orc.silu(G) * U
+    bound = 1.1 * gamma * AG * np.abs(U) + (np.abs(G) + 0.3) * gamma * AU + 1e-6 * np.abs(H) + 1e-30
+    err = np.abs(gu.f64(h_dev) - H)
+    bad = err > bound
+    assert not bad.any(), f"H: {bad.sum()} of {bad.size} off, worst excess {(err - bound).max():.3e}"
+
+
+def _check_y(y_dev, Hd, Wd):
+    gamma = Hd.shape[1] * 2.0 ** -24
+    Y = Hd @ Wd.T
+    bound = gamma * (np.abs(Hd) @ np.abs(Wd).T) + 1e-30
+    err = np.abs(gu.f64(y_dev) - Y)
+    bad = err > bound
+    assert not bad.any(), f"Y: {bad.sum()} of {bad.size} off, worst excess {(err - bound).max():.3e}"
+
+
+def _oracle_mx_layer(inp, wts, logits, k):
+    """The oracle's MX layer on the device's logits (routing) and weight codes."""
+    E = inp.cfg.E
+    idx, w, _ = orc.route(logits, k)
+    off, row_of, row_src = orc.permute(idx, E)
+    xq, xs = mx.quantize(gu.f64(inp.x), mx.E4M3)
+    Y = np.zeros((inp.cfg.T * k, inp.cfg.d))
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        rows = row_src[lo:hi]
+        H = orc.silu(mx.dequantize(xq[rows], xs[rows], mx.E4M3) @ _deq_w(wts[0], e).T) * \
+            (mx.dequantize(xq[rows], xs[rows], mx.E4M3) @ _deq_w(wts[1], e).T)
+        hq, hs = mx.quantize(H, mx.E4M3)
+        Y[lo:hi] = mx.dequantize(hq, hs, mx.E4M3) @ _deq_w(wts[2], e).T
+    return orc.combine(Y, row_of, w)
+
+
+CASES = {
+    "small": dict(T=64, d=512, E=8, k=2, h=512),
+    "ragged": dict(T=300, d=1024, E=24, k=4, h=512),
+    "many_tiles": dict(T=700, d=512, E=3, k=2, h=1024),
+    "empty_experts": dict(T=20, d=512, E=64, k=1, h=512),
+    "k_equals_E": dict(T=9, d=512, E=4, k=4, h=512),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_mx_forward_matches_oracle(dev, moe, case):
+    cfg = scaled_config("tiny", name=f"mx_{case}", seed=100 + len(case), **CASES[case])
+    print(f"mx case {case}: {cfg}", flush=True)
+    inp = make_inputs(cfg)
+    di = inp.to(dev)
+    wts = _mx_weights(moe, di, dev)
+    fwd = moe.MXForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
+    out = fwd(di.x, di.w_router, di.router_bias, *wts)
+    torch.cuda.synchronize()
+    it = fwd.intermediate
+    idx_ref, _ = gu.check_route(it("logits"), it("topk_idx"), it("topk_w"), cfg.k)
+    off, row_of, row_src = gu.check_permutation(it("expert_offsets"), it("row_of"), it("row_src"), idx_ref, cfg.E)
+    xq_ref, xs_ref = mx.quantize(gu.f64(inp.x), mx.E4M3)
+    assert np.array_equal(_u8(it("x_q")), xq_ref) and np.array_equal(_u8(it("x_s")), xs_ref)
+    Xd = mx.dequantize(_u8(it("x_q")), _u8(it("x_s")), mx.E4M3)
+    h_act = it("h_act")
+    hq_ref, hs_ref = mx.quantize(gu.f64(h_act), mx.E4M3)
+    assert np.array_equal(_u8(it("h_q")), hq_ref), "H codes differ from the oracle's on the device's H"
+    assert np.array_equal(_u8(it("h_s")), hs_ref)
+    Hd = mx.dequantize(_u8(it("h_q")), _u8(it("h_s")), mx.E4M3)
+    for e in range(cfg.E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        _check_h(h_act[lo:hi], Xd[row_src[lo:hi]], _deq_w(wts[0], e), _deq_w(wts[1], e))
+        _check_y(it("y_rows")[lo:hi], Hd[lo:hi], _deq_w(wts[2], e))
+    # combine of the device's own rows
+    y = gu.f64(it("y_rows"))
+    w = gu.f64(it("topk_w"))
+    ref = orc.combine(y, row_of, w)
+    bound = (cfg.k + 1) * 2.0 ** -23 * sum(np.abs(w[:, j:j + 1] * y[row_of[:, j]]) for j in range(cfg.k)) + 1e-30
+    assert np.all(np.abs(gu.f64(out) - ref) <= bound)
+    # end to end against the oracle's own MX layer
+    gu.check_layer(out, _oracle_mx_layer(inp, wts, gu.f64(it("logits")), cfg.k), "MX out")
+    # and within the quantisation error of the bf16 layer
+    plain = orc.forward(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down, cfg.k,
+                        logits=gu.f64(it("logits")))["out"]
+    rel = np.abs(gu.f64(out) - plain).max() / np.abs(plain).max()
+    print(f"mx case {case}: max normwise difference from the bf16 layer {rel:.3f}", flush=True)
+    assert rel < 0.35
+
+
+def test_mx_forward_deterministic(dev, moe):
+    cfg = scaled_config("tiny", name="mx_det", T=200, d=512, E=16, k=4, h=512)
+    di = make_inputs(cfg).to(dev)
+    wts = _mx_weights(moe, di, dev)
+    fwd = moe.MXForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
+    a = fwd(di.x, di.w_router, None, *wts).clone()
+    b = fwd(di.x, di.w_router, None, *wts)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.slow
+def test_mx_prefill_full_size_sampled(dev, moe):
+    """The prefill layer (T = 8192, d = 7168, E = 256, top-4, h = 2048) with MXFP4 experts:
+    routing and permutation bit for bit, x's codes bit for bit, sampled weight rows' codes
+    bit for bit, and the H, Y and out rows of sampled tokens against the oracle."""
+    from synthetic import CONFIGS
+    cfg = CONFIGS["prefill"]
+    print("mx prefill: drawing inputs", flush=True)
+    inp = make_inputs(cfg, device=dev)
+    wts = _mx_weights(moe, inp, dev)
+    fwd = moe.MXForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
+    out = fwd(inp.x, inp.w_router, None, *wts)
+    torch.cuda.synchronize()
+    print("mx prefill: forward done", flush=True)
+    it = fwd.intermediate
+    idx_ref, _ = gu.check_route(it("logits"), it("topk_idx"), it("topk_w"), cfg.k)
+    off, row_of, row_src = gu.check_permutation(it("expert_offsets"), it("row_of"), it("row_src"), idx_ref, cfg.E)
+    xq_ref, xs_ref = mx.quantize(gu.f64(inp.x), mx.E4M3)
+    assert np.array_equal(_u8(it("x_q")), xq_ref) and np.array_equal(_u8(it("x_s")), xs_ref)
+    Xd = mx.dequantize(xq_ref, xs_ref, mx.E4M3)
+    r = np.random.default_rng(7)
+    tokens = [0, 4321, cfg.T - 1]
+    y = it("y_rows")
+    w = gu.f64(it("topk_w"))
+    for t in tokens:
+        acc = np.zeros(cfg.d)
+        for j in range(cfg.k):
+            e, row = int(idx_ref[t, j]), int(row_of[t, j])
+            for pair, name in ((wts[0], "gate"), (wts[1], "up"), (wts[2], "down")):
+                src = {"gate": inp.w_gate, "up": inp.w_up, "down": inp.w_down}[name][e]
+                rows = r.choice(src.shape[0], size=8, replace=False)
+                cref, sref = mx.quantize(gu.f64(src[rows]), mx.E2M1)
+                assert np.array_equal(unpack_fp4(pair[0][e][rows]), cref), f"{name} codes of expert {e}"
+                assert np.array_equal(unswizzle_scales(pair[1][e][rows]), sref), f"{name} scales of expert {e}"
+            _check_h(it("h_act")[row:row + 1], Xd[t:t + 1], _deq_w(wts[0], e), _deq_w(wts[1], e))
+            hq, hs = it("h_q")[row:row + 1], it("h_s")[row:row + 1]
+            Hd = mx.dequantize(_u8(hq), _u8(hs), mx.E4M3)
+            _check_y(y[row:row + 1], Hd, _deq_w(wts[2], e))
+            acc += w[t, j] * gu.f64(y[row])
+        err = np.abs(gu.f64(out[t]) - acc).max()
+        assert err <= 1e-5 * np.abs(acc).max() + 1e-30, (t, err)
