@@ -50,6 +50,9 @@ def parse():
                          "'latent' times the Stable LatentMoE layer instead)")
     ap.add_argument("--cpu-experts", type=int, default=128,
                     help="experts the CPU oracle runs in its bounded sample (0 = skip the CPU baseline)")
+    ap.add_argument("--experts", choices=["bf16", "mxfp4"], default="bf16",
+                    help="expert weight format: bf16, or MXFP4 weights with MXFP8 activations (weights quantised "
+                         "once before the timed steps)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, run a plain float32 copy kernel (out = -in) over this many MiB three "
                          "times, so that a counter run can scale FETCH_SIZE / WRITE_SIZE by a known byte count")
@@ -171,6 +174,118 @@ class Balance:
             gbs = nbytes[name] / (t * 1e-6) / 1e9
             out[name] = {"us": t, "bytes": nbytes[name], "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
         return out
+
+
+class MXLayer:
+    """The routed layer with MXFP4 experts: preallocated buffers and C-ABI calls."""
+
+    def __init__(self, lib, inp, cfg, dev):
+        import torch
+
+        from sparse_mixture_experts_fp32_amd import ops
+        self.lib, self.inp, self.cfg, self.dev = lib, inp, cfg, dev
+        T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
+        n = T * k
+        e = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+        u8 = torch.uint8
+        self.gate = ops.moe_mx_quantize_weights(inp.w_gate)
+        self.up = ops.moe_mx_quantize_weights(inp.w_up)
+        self.down = ops.moe_mx_quantize_weights(inp.w_down)
+        self.logits, self.idx, self.w = e(T, E, dt=torch.float32), e(T, k, dt=torch.int32), e(T, k, dt=torch.float32)
+        self.offsets, self.row_of, self.row_src = e(E + 1, dt=torch.int32), e(T, k, dt=torch.int32), e(n, dt=torch.int32)
+        self.x_q, self.x_s = e(T, d, dt=u8), e(T, d // 32, dt=u8)
+        self.h_act, self.h_q, self.h_s = e(n, h, dt=torch.float32), e(n, h, dt=u8), e(n, h // 32, dt=u8)
+        self.y_rows, self.out = e(n, d, dt=torch.float32), e(T, d, dt=torch.float32)
+        self.shape = lib.shape(T, d, E, k, h)
+        self.ws_route = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_ROUTE)), dt=u8)
+        self.ws_perm = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_PERMUTE)), dt=u8)
+        self.ws_ffn = e(max(1, lib.workspace_bytes(self.shape, lib.MOE_CALL_EXPERT_FFN)), dt=u8)
+        self.stream = torch.cuda.current_stream(dev)
+        self.P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        self.sh = ctypes.byref(self.shape)
+        self.sp = ctypes.c_void_p(self.stream.cuda_stream)
+
+    def step(self, ev=None):
+        L, P, sh, sp, i, c = self.lib.lib, self.P, self.sh, self.sp, self.inp, self.lib.check
+        T, d, h, n = self.cfg.T, self.cfg.d, self.cfg.h, self.cfg.T * self.cfg.k
+        c(L.moe_route(sh, P(i.x), P(i.w_router), P(i.router_bias), P(self.logits), P(self.idx), P(self.w),
+                      P(self.ws_route), self.ws_route.numel(), sp))
+        c(L.moe_permute(sh, None, P(self.idx), P(self.offsets), P(self.row_of), P(self.row_src), None,
+                        P(self.ws_perm), self.ws_perm.numel(), sp))
+        c(L.moe_mx_quantize_rows(T, d, P(i.x), 0, P(self.x_q), P(self.x_s), sp))
+        if ev is not None:
+            ev[0].record(self.stream)
+        c(L.moe_mx_expert_gate_up(sh, P(self.x_q), P(self.x_s), P(self.row_src), P(self.offsets), P(self.gate[0]),
+                                  P(self.gate[1]), P(self.up[0]), P(self.up[1]), P(self.h_act), P(self.ws_ffn),
+                                  self.ws_ffn.numel(), sp))
+        if ev is not None:
+            ev[1].record(self.stream)
+        c(L.moe_mx_quantize_rows(n, h, P(self.h_act), 1, P(self.h_q), P(self.h_s), sp))
+        if ev is not None:
+            ev[2].record(self.stream)
+        c(L.moe_mx_expert_down(sh, P(self.h_q), P(self.h_s), P(self.offsets), P(self.down[0]), P(self.down[1]),
+                               P(self.y_rows), P(self.ws_ffn), self.ws_ffn.numel(), sp))
+        if ev is not None:
+            ev[3].record(self.stream)
+        c(L.moe_combine(sh, P(self.y_rows), P(self.row_of), P(self.w), P(self.out), sp))
+
+
+def mx_bench(args, lib, inp, cfg, dev, note):
+    """Timed steps of the MXFP4-expert layer; returns the JSON result."""
+    import torch
+
+    from sparse_mixture_experts_fp32_amd import MXForward
+    layer = MXLayer(lib, inp, cfg, dev)
+    torch.cuda.synchronize()
+    note("expert weights quantised to MXFP4")
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    note(f"{args.warmup} warmup steps done")
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        layer.step(evs[s])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    note(f"{K} timed steps done")
+    gate_up_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    hq_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    down_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    fwd = MXForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
+    ref = fwd(inp.x, inp.w_router, inp.router_bias, layer.gate, layer.up, layer.down)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, layer.out), "bench step and moe_mx_forward disagree"
+    del fwd, ref
+    note("bench step equals moe_mx_forward bit for bit")
+    T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
+    n = T * k
+    counts = (layer.offsets[1:] - layer.offsets[:-1]).cpu()
+    touched = int((counts > 0).sum())
+    # algorithmic bytes of the MX gate/up pass: one E4M3 row (+ scales) per assignment,
+    # the touched experts' E2M1 gate and up weights (+ scales) once, H written in float32
+    w_bytes = lambda N, Kd: N * (Kd / 2 + Kd / 32)  # noqa: E731
+    gu_bytes = n * (d + d / 32) + 2.0 * touched * w_bytes(h, d) + 4.0 * n * h
+    gu_gbs = gu_bytes / (gate_up_ms * 1e-3) / 1e9
+    dn_bytes = n * (h + h / 32) + touched * w_bytes(d, h) + 4.0 * n * d
+    flops = 6.0 * n * d * h
+    return {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8xfp4", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} top-{k} h={h}, SwiGLU experts in MXFP4 with MXFP8 "
+                               f"activations, fp32 gate", "T": T, "d": d, "E": E, "k": k, "h": h, "seed": cfg.seed,
+                   "experts_touched": touched},
+        "grouped_gemm": {"ms": gate_up_ms + down_ms, "tflops": flops / ((gate_up_ms + down_ms) * 1e-3) / 1e12,
+                         "mfma_frac_fp8": flops / ((gate_up_ms + down_ms) * 1e-3) / 1e12 / 5000.0,
+                         "gate_up_ms": gate_up_ms, "h_quantise_ms": hq_ms, "down_ms": down_ms,
+                         "down_gbs": dn_bytes / (down_ms * 1e-3) / 1e9},
+        "roofline": {"kernel": "mx_grouped_kernel<gated> (MX gate/up pass + SwiGLU)", "bound": "hbm",
+                     "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes": gu_bytes},
+    }
 
 
 def cpu_baseline(inp, cfg, n_experts):
@@ -340,6 +455,58 @@ def latent_cpu_baseline(inp, cfg, n_tokens):
                        f"scaled by {cfg.T / n_tokens:.0f} to {layer_s:.0f} s per layer")}
 
 
+def mx_cpu_baseline(inp, cfg, n_experts):
+    """The MX oracle on the host cores: gate logits, routing, permutation and the MXFP8
+    quantisation of x over every token, then n_experts evenly spaced experts (their
+    weights quantised to MXFP4, their rows through the MX SwiGLU FFN), that time scaled
+    by rows; the combine over every token."""
+    import numpy as np
+
+    import oracle.moe_oracle as orc
+    import oracle.mx as mx
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = os.cpu_count()
+    E, k = cfg.E, cfg.k
+    x_h, wr_h = inp.x.cpu(), inp.w_router.cpu()
+    b_h = None if inp.router_bias is None else inp.router_bias.cpu()
+    sample = sorted({int(round(i * E / n_experts)) % E for i in range(n_experts)})
+    wts = {e: (inp.w_gate[e].cpu(), inp.w_up[e].cpu(), inp.w_down[e].cpu()) for e in sample}
+    t = {}
+    t0 = time.perf_counter()
+    L = orc.gate_logits(x_h, wr_h, b_h)
+    idx, w, _ = orc.route(L, k)
+    off, row_of, row_src = orc.permute(idx, E)
+    xq, xs = mx.quantize(x_h, mx.E4M3)
+    t["routing_and_x"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    Y = np.zeros((cfg.T * k, cfg.d))
+    for e in sample:
+        gq, gs = mx.quantize(wts[e][0], mx.E2M1)
+        uq, us = mx.quantize(wts[e][1], mx.E2M1)
+        dq, ds = mx.quantize(wts[e][2], mx.E2M1)
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = row_src[lo:hi]
+        H = mx.mx_expert_gate_up(xq[rows], xs[rows], gq, gs, uq, us)
+        hq, hs = mx.quantize(H, mx.E4M3)
+        Y[lo:hi] = mx.mx_expert_down(hq, hs, dq, ds)
+    t["ffn_sample"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.combine(Y, row_of, w)
+    t["combine"] = time.perf_counter() - t0
+    rows_all = int(off[-1])
+    rows_sample = int(sum(off[e + 1] - off[e] for e in sample))
+    scale = E / len(sample)  # each expert's weights are quantised whatever its row count
+    layer_s = t["routing_and_x"] + t["combine"] + t["ffn_sample"] * scale
+    return {"value": cfg.T / layer_s, "unit": "tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": (f"{cfg.name} workload with MXFP4 experts, float64 numpy oracle: gate logits, routing, "
+                       f"permutation, MXFP8 quantisation of x and combine over all {cfg.T} tokens; {len(sample)} of "
+                       f"{E} experts quantised and run ({rows_sample} of {rows_all} rows), that time scaled by "
+                       f"{scale:.0f}; {sum(t.values()):.1f} s measured, {layer_s:.0f} s estimated per layer")}
+
+
 def measured_traffic(workload):
     """HBM bytes per gate/up launch from the committed counter record, or None if the kernel changed since."""
     import hashlib
@@ -387,8 +554,15 @@ def main():
     inp = make_inputs(cfg, device=dev, progress=progress)
     print(f"[bench] {cfg.name}: inputs ready", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
-    layer = Layer(lib, inp, cfg, dev)
     note = lambda msg: print(f"[bench] {cfg.name}: {msg}", file=sys.stderr, flush=True)  # noqa: E731
+    if args.experts == "mxfp4":
+        result = mx_bench(args, lib, inp, cfg, dev, note)
+        if args.cpu_experts > 0:
+            note("timing the CPU oracle on a bounded sample")
+            result["cpu_baseline"] = mx_cpu_baseline(inp, cfg, min(args.cpu_experts, 4))
+        print(json.dumps(result), flush=True)
+        return
+    layer = Layer(lib, inp, cfg, dev)
     note("buffers allocated")
 
     if args.copy_probe_mib > 0:

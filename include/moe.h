@@ -414,6 +414,16 @@ int moe_mx_expert_ffn(const moe_shape_t* shape, const uint8_t* a_q, const uint8_
                       const uint8_t* wd_s, float* h_act, uint8_t* h_q, uint8_t* h_s, float* y_rows,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of moe_mx_expert_ffn (with the H quantisation, moe_mx_quantize_rows on
+ * h_act, in between), for callers that time or overlap them; same arguments and workspace. */
+int moe_mx_expert_gate_up(const moe_shape_t* shape, const uint8_t* a_q, const uint8_t* a_s,
+                          const int32_t* a_rows, const int32_t* expert_offsets, const uint8_t* wg_q,
+                          const uint8_t* wg_s, const uint8_t* wu_q, const uint8_t* wu_s, float* h_act,
+                          void* ws, size_t ws_bytes, void* stream);
+int moe_mx_expert_down(const moe_shape_t* shape, const uint8_t* h_q, const uint8_t* h_s,
+                       const int32_t* expert_offsets, const uint8_t* wd_q, const uint8_t* wd_s,
+                       float* y_rows, void* ws, size_t ws_bytes, void* stream);
+
 /* Intermediates moe_mx_forward leaves in its workspace (moe_mx_forward_ws_offset). */
 typedef enum moe_mx_slot {
     MOE_MX_LOGITS = 0,         /* [T, E] float32 */

@@ -83,6 +83,8 @@ def _load():
         "moe_mx_quantize_weights": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
         "moe_mx_quantize_rows": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32, P, P, P]),
         "moe_mx_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_mx_expert_gate_up": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_mx_expert_down": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_mx_forward_ws_offset": (ctypes.c_int, [S, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_mx_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
     }

@@ -757,6 +757,58 @@ int moe_mx_expert_ffn(const moe_shape_t* shape, const uint8_t* a_q, const uint8_
     return hip_status(err, "mx down launch");
 }
 
+int moe_mx_expert_gate_up(const moe_shape_t* shape, const uint8_t* a_q, const uint8_t* a_s, const int32_t* a_rows,
+                          const int32_t* expert_offsets, const uint8_t* wg_q, const uint8_t* wg_s,
+                          const uint8_t* wu_q, const uint8_t* wu_s, float* h_act, void* ws, size_t ws_bytes,
+                          void* stream) {
+    int st = check_mx_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(a_q);
+    MOE_CHECK_PTR(a_s);
+    if (a_rows != nullptr && !aligned16(a_rows)) return fail(MOE_ERR_INVALID_ARG, "a_rows is not 16-byte aligned");
+    MOE_CHECK_PTR(expert_offsets);
+    MOE_CHECK_PTR(wg_q);
+    MOE_CHECK_PTR(wg_s);
+    MOE_CHECK_PTR(wu_q);
+    MOE_CHECK_PTR(wu_s);
+    MOE_CHECK_PTR(h_act);
+    st = check_ws(ws, ws_bytes, ffn_ws(shape));
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = shape->T * shape->k;
+    const FfnWs fw = ffn_carve(shape, ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_mx_ffn_pass(true, a_q, a_s, a_rows, a_rows ? shape->T : n, fw.tiles, fw.tile_start, n,
+                                  shape->E, wg_q, wg_s, wu_q, wu_s, shape->h, shape->d, h_act, s);
+    return hip_status(err, "mx gate_up launch");
+}
+
+int moe_mx_expert_down(const moe_shape_t* shape, const uint8_t* h_q, const uint8_t* h_s,
+                       const int32_t* expert_offsets, const uint8_t* wd_q, const uint8_t* wd_s, float* y_rows,
+                       void* ws, size_t ws_bytes, void* stream) {
+    int st = check_mx_shape(shape);
+    if (st != MOE_OK) return st;
+    if (shape->T == 0) return ok();
+    MOE_CHECK_PTR(h_q);
+    MOE_CHECK_PTR(h_s);
+    MOE_CHECK_PTR(expert_offsets);
+    MOE_CHECK_PTR(wd_q);
+    MOE_CHECK_PTR(wd_s);
+    MOE_CHECK_PTR(y_rows);
+    st = check_ws(ws, ws_bytes, ffn_ws(shape));
+    if (st != MOE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t n = shape->T * shape->k;
+    const FfnWs fw = ffn_carve(shape, ws);
+    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
+    if (err != hipSuccess) return hip_status(err, "build_tiles launch");
+    err = moe::launch_mx_ffn_pass(false, h_q, h_s, nullptr, n, fw.tiles, fw.tile_start, n, shape->E, wd_q, wd_s,
+                                  nullptr, nullptr, shape->d, shape->h, y_rows, s);
+    return hip_status(err, "mx down launch");
+}
+
 int moe_mx_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset) {
     int st = check_mx_shape(shape);
     if (st != MOE_OK) return st;

@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
               "moe_qb_route", "moe_qb_histogram", "moe_qb_update", "moe_latent_forward",
               "moe_latent_workspace_bytes", "moe_latent_ws_offset", "moe_combine_rmsnorm",
               "moe_mx_quantize_weights", "moe_mx_quantize_rows", "moe_mx_expert_ffn", "moe_mx_forward",
-              "moe_mx_forward_ws_offset"]:
+              "moe_mx_forward_ws_offset", "moe_mx_expert_gate_up", "moe_mx_expert_down"]:
         assert n in names
 
 
@@ -251,6 +251,8 @@ def test_mx_calls_check_arguments(lib):
     assert L.moe_mx_forward(ctypes.byref(s), a, a, None, a, None, a, a, a, a, a, a, need, None) == 1
     assert L.moe_mx_expert_ffn(ctypes.byref(s), a, a, None, a, a, a, a, a, a, a, a, None, a, a, a, 1 << 20,
                                None) == 1
+    assert L.moe_mx_expert_gate_up(ctypes.byref(s), a, a, None, a, a, a, a, a, None, a, 1 << 20, None) == 1
+    assert L.moe_mx_expert_down(ctypes.byref(s), a, a, a, a, a, a, a, 10, None) == 3
     assert L.moe_mx_quantize_weights(2, 16, 256, a, a, a, None) == 1       # K not a multiple of 512
     assert L.moe_mx_quantize_weights(2, 16, 512, None, a, a, None) == 1
     assert L.moe_mx_quantize_weights(0, 16, 512, None, None, None, None) == 0
