@@ -20,14 +20,15 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "select.h"
 
 namespace moe {
 
 // ------------------------------------------------------------ QB selection
 //
 // One wavefront per token, as in the plain top-k: 64-bit keys (ordered float
-// bits of s + b, then ~id), k + 1 rounds of a wavefront max. Lanes 0..k-1 end
-// with the chosen ids in slot order and lane k with the cutoff. The weights
+// bits of s + b, then ~id), the k + 1 largest selected by select_top. Lanes
+// 0..k-1 end with the chosen ids in slot order and lane k with the cutoff. The weights
 // use the unbiased logits of the chosen experts: exp(s_j - M) / sum_i exp(s_i - M),
 // M their maximum (the softmax denominator over all E cancels).
 
@@ -36,6 +37,7 @@ __global__ __launch_bounds__(256) void qb_select_kernel(const float* __restrict_
                                                         const float* __restrict__ bias, int64_t T, int E, int k,
                                                         int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
                                                         float* __restrict__ alpha) {
+    __shared__ uint64_t sel[4][kSelectLds];
     const int lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (t >= T) return;  // whole wavefront
@@ -49,21 +51,10 @@ __global__ __launch_bounds__(256) void qb_select_kernel(const float* __restrict_
                             (0xffffffffu - static_cast<uint32_t>(e)))
                          : 0ull;
     }
-    int my_id = 0;
-    float my_score = 0.f;
-    for (int j = 0; j <= k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-#pragma unroll
-        for (int i = 0; i < NPER; ++i)
-            if (key[i] == best) key[i] = 0ull;
-        if (lane == j) {
-            my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
-            my_score = key_value(static_cast<uint32_t>(best >> 32));
-        }
-    }
+    // lane j <= k: the j-th largest biased key (lane k: the cutoff)
+    const uint64_t best = select_top<NPER>(key, k + 1, sel[threadIdx.x >> 6]);
+    const int my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+    const float my_score = key_value(static_cast<uint32_t>(best >> 32));
     const bool chosen = lane < k;
     // my_id < E always: k + 1 <= E valid keys exist and padding keys are 0
     const float s = chosen ? row[my_id] : -INFINITY;

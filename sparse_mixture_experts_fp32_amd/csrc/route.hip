@@ -5,6 +5,7 @@
 // Frontier", section "Mixture-of-Experts with Dynamic Load Balancing".
 #include "device_common.h"
 #include "launch.h"
+#include "select.h"
 
 #include <algorithm>
 
@@ -147,8 +148,9 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __rest
 // One wavefront per token; lane l holds experts l, l + 64, ... Each logit
 // becomes a 64-bit key whose upper half orders the float value (-0.0 folded
 // onto +0.0, NaN below everything) and whose lower half is ~expert id, so the
-// largest key is the largest logit with ties going to the lower id. k rounds of
-// a wavefront max pick the slots in descending order.
+// largest key is the largest logit with ties going to the lower id. select_top
+// (select.h) leaves the j-th largest key in lane j: a threshold from the lane
+// maxima prunes the candidates, which are then ranked in LDS.
 //
 // Renormalised weights: p_j / sum_{i<k} p_i with p = softmax over all E equals
 // exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0): the softmax denominator cancels,
@@ -159,6 +161,7 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
                                                            int64_t T, int E, int k,
                                                            int32_t* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w) {
+    __shared__ uint64_t sel[4][kSelectLds];
     const int lane = threadIdx.x & 63;
     const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -171,22 +174,10 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
         key[i] = (e < E) ? ((static_cast<uint64_t>(order_key(row[e])) << 32) | (0xffffffffu - static_cast<uint32_t>(e)))
                          : 0ull;
     }
-
-    int my_id = 0;
-    float my_val = 0.f;
-    for (int j = 0; j < k; ++j) {
-        uint64_t best = key[0];
-#pragma unroll
-        for (int i = 1; i < NPER; ++i) best = key[i] > best ? key[i] : best;
-        best = wave_max_u64(best);
-#pragma unroll
-        for (int i = 0; i < NPER; ++i)
-            if (key[i] == best) key[i] = 0ull;  // unique: the low half names one expert
-        if (lane == j) {
-            my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
-            my_val = key_value(static_cast<uint32_t>(best >> 32));
-        }
-    }
+    // lane j < k: the j-th largest key
+    const uint64_t best = select_top<NPER>(key, k, sel[threadIdx.x >> 6]);
+    const int my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
+    const float my_val = key_value(static_cast<uint32_t>(best >> 32));
     const float top = __shfl(my_val, 0, kWave);
     const float ex = (lane < k) ? expf(my_val - top) : 0.f;
     const float sum = wave_sum_f32(ex);
