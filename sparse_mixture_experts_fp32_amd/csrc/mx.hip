@@ -187,22 +187,22 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
         for (int i = 0; i < kMB; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / kMxKS;  // a multiple of 4
-    u32x4 a_reg[kPasses];
-    uint32_t s_reg = 0u;
-    auto load_a = [&](int s) {
+    u32x4 ar[2][kPasses];      // A rows, two K steps ahead
+    uint32_t sr[2] = {0u, 0u}; // their scale words
+    auto load_a = [&](u32x4 (&dst)[kPasses], uint32_t& sdst, int s) {
 #pragma unroll
-        for (int p = 0; p < kPasses; ++p) a_reg[p] = *reinterpret_cast<const u32x4*>(A + a_off[p] + s * kMxKS);
-        if (s_on) s_reg = *reinterpret_cast<const uint32_t*>(As + s_off + s * 4);
+        for (int p = 0; p < kPasses; ++p) dst[p] = *reinterpret_cast<const u32x4*>(A + a_off[p] + s * kMxKS);
+        if (s_on) sdst = *reinterpret_cast<const uint32_t*>(As + s_off + s * 4);
     };
-    auto store_a = [&](int buf) {
+    auto store_a = [&](int buf, const u32x4 (&src)[kPasses], uint32_t ssrc) {
 #pragma unroll
         for (int p = 0; p < kPasses; ++p)
             *reinterpret_cast<u32x4*>(sA + buf * kBufA + (p * kMxRowsPerPass + a_row) * kMxARow + a_chunk * 16) =
-                a_reg[p];
-        if (s_on) sS[buf * kBufS + tid] = s_reg;
+                src[p];
+        if (s_on) sS[buf * kBufS + tid] = ssrc;
     };
-    u32x4 bq[2][kMxNB];
-    uint32_t bs[2][kMxNB];
+    u32x4 bq[4][kMxNB];        // weights, a ring of four K steps (three ahead)
+    uint32_t bs[2][kMxNB];     // weight scale words, two sets of four K steps
     auto load_b = [&](u32x4 (&dst)[kMxNB], int s) {
 #pragma unroll
         for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const u32x4*>(wq[b] + s * (kMxKS / 2));
@@ -211,7 +211,7 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
 #pragma unroll
         for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const uint32_t*>(wsc[b] + q4 * 16);
     };
-    // multiply one K step from LDS buffer `buf` with weights w and the scale word sel
+    // multiply one K step from LDS buffer `buf` with weights w and scale byte sel of words ws
     auto step = [&](int buf, const u32x4 (&w)[kMxNB], const uint32_t (&ws)[kMxNB], auto sel) {
         constexpr int kSel = decltype(sel)::value;
         v8i bop[kMxNB];
@@ -234,25 +234,29 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
         }
     };
 
-    load_a(0);
+    load_a(ar[0], sr[0], 0);
+    load_a(ar[1], sr[1], min(1, nk - 1));
     load_b(bq[0], 0);
+    load_b(bq[1], min(1, nk - 1));
+    load_b(bq[2], min(2, nk - 1));
     load_bs(bs[0], 0);
-    store_a(0);
+    store_a(0, ar[0], sr[0]);
     __syncthreads();
-    // Eight steps per trip: steps 0-3 use scale word set 0 (word s0 / 4), steps 4-7
-    // set 1 (word s0 / 4 + 1); each set is loaded four steps before it is used, so
-    // every register index is a compile-time constant. Step U: load A rows and
-    // weights of the next step, multiply this one (scale byte U % 4), store the
-    // next A rows in the other LDS buffer, barrier.
-#define MOE_MX_STEP(U, SET)                                                                     \
-    {                                                                                           \
-        const int s = s0 + (U);                                                                 \
-        const int sn = min(s + 1, nk - 1);                                                      \
-        load_a(sn);                                                                             \
-        load_b(bq[((U) + 1) & 1], sn);                                                          \
-        if (wave_on) step((U) & 1, bq[(U) & 1], bs[SET], std::integral_constant<int, (U) % 4>{}); \
-        store_a(((U) + 1) & 1);                                                                 \
-        __syncthreads();                                                                        \
+    // Eight steps per trip (every register index a compile-time constant): steps
+    // 0-3 use scale word set 0 (word s0 / 4), steps 4-7 set 1 (word s0 / 4 + 1),
+    // each set loaded four steps before it is used. Step U: load A rows of step
+    // s + 2, then weights of step s + 3 (vector-memory counters retire in issue
+    // order, so waiting for the A rows of s + 1 never waits for later weights),
+    // multiply step s (scale byte U % 4), store the A rows of s + 1 in the other
+    // LDS buffer, barrier.
+#define MOE_MX_STEP(U, SET)                                                                           \
+    {                                                                                                 \
+        const int s = s0 + (U);                                                                       \
+        load_a(ar[(U) % 2], sr[(U) % 2], min(s + 2, nk - 1));                                         \
+        load_b(bq[((U) + 3) % 4], min(s + 3, nk - 1));                                                \
+        if (wave_on) step((U) % 2, bq[(U) % 4], bs[SET], std::integral_constant<int, (U) % 4>{});     \
+        store_a(((U) + 1) % 2, ar[((U) + 1) % 2], sr[((U) + 1) % 2]);                                 \
+        __syncthreads();                                                                              \
     }
     for (int s0 = 0; s0 < nk; s0 += 8) {
         load_bs(bs[1], min(s0 / 4 + 1, nk / 4 - 1));
@@ -265,16 +269,28 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
 #undef MOE_MX_STEP
 
     if (!wave_on) return;
+    // Every value first, then the stores back to back: a store reads its data and
+    // address registers after issue, so interleaving each store with the next
+    // value's arithmetic would make the compiler wait for every store to finish.
+    if (kGated) {  // H row (float32): gate block 0, up block 1
+#pragma unroll
+        for (int i = 0; i < kMB; ++i)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const float g = acc[0][i][qq], u = acc[1][i][qq];
+                acc[0][i][qq] = g / (1.0f + __expf(-g)) * u;
+            }
+    }
+    float* cbase = C + row0 * N + n_wave + fr;
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
             const int r = i * 16 + 4 * fg + qq;
             if (r >= M) continue;
-            float* crow = C + (row0 + r) * N + n_wave + fr;
-            if (kGated) {  // H row (float32): gate block 0, up block 1
-                const float g = acc[0][i][qq], u = acc[1][i][qq];
-                crow[0] = g / (1.0f + __expf(-g)) * u;
+            float* crow = cbase + static_cast<int64_t>(r) * N;
+            if (kGated) {
+                crow[0] = acc[0][i][qq];
             } else {
 #pragma unroll
                 for (int b = 0; b < kMxNB; ++b) crow[16 * b] = acc[b][i][qq];
