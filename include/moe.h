@@ -382,14 +382,18 @@ int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int
  * The MX calls need d and h to be multiples of 512.
  *
  * Layouts:
- *  - MXFP4 weights of G matrices [N, K]: codes [G, N, K/2] bytes, element 2i of
- *    a row in the low nibble of byte i; scales [G, N, K/32] bytes in the
- *    matrix-core order: the scale of block kb of row n sits at byte
- *    n*(K/32) + (kb/16)*16 + (kb%4)*4 + (kb/4)%4 of its matrix.
+ *  - MXFP4 weights of G matrices [N, K] (N a multiple of 16), in matrix-core
+ *    order, rows n counted within a matrix:
+ *    codes, G * N * K/2 bytes: the 16 bytes of block kb (32 elements, element
+ *    2i in the low nibble of byte i) of row n sit at byte
+ *    ((n/16) * (K/128) + kb/4) * 1024 + (n%16) * 64 + (kb%4) * 16, so each
+ *    16-row x 128-column tile is one contiguous kilobyte;
+ *    scales, G * N * K/32 bytes: the scale of block kb of row n sits at byte
+ *    ((n/16) * (K/512) + kb/16) * 256 + (n%16) * 16 + (kb%4) * 4 + (kb/4)%4.
  *  - MXFP8 rows [R, K]: codes [R, K] bytes; scales [R, K/32] bytes in row order.
  */
 
-/* Quantise bf16 weights w [groups, N, K] to MXFP4 (K a multiple of 512). */
+/* Quantise bf16 weights w [groups, N, K] to MXFP4 (K a multiple of 512, N of 16). */
 int moe_mx_quantize_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint8_t* q,
                             uint8_t* scales, void* stream);
 

@@ -690,8 +690,8 @@ int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const
 
 int moe_mx_quantize_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint8_t* q, uint8_t* scales,
                             void* stream) {
-    if (groups < 0 || N < 0 || K < 512 || K % 512 != 0 || K > (1 << 20))
-        return fail(MOE_ERR_INVALID_ARG, "bad weight shape (groups %lld, N %d, K %d; K a multiple of 512)",
+    if (groups < 0 || N < 0 || N % 16 != 0 || K < 512 || K % 512 != 0 || K > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "bad weight shape (groups %lld, N %d, K %d; N a multiple of 16, K of 512)",
                     static_cast<long long>(groups), N, K);
     if (groups * N * static_cast<int64_t>(K / 32) >= (int64_t(1) << 40))
         return fail(MOE_ERR_UNSUPPORTED, "weights too large");

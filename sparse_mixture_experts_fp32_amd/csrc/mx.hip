@@ -31,6 +31,7 @@ namespace moe {
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kMxBlock = 32;
+constexpr int kMxKStep = 128;  // K of one MFMA
 constexpr int kXcdsMx = 8;  // workgroup ids are dealt to the 8 XCDs round-robin
 
 // ------------------------------------------------------------ conversion
@@ -74,16 +75,26 @@ __device__ __forceinline__ float load_elem<uint16_t>(const uint16_t* p) { return
 template <>
 __device__ __forceinline__ float load_elem<float>(const float* p) { return *p; }
 
-// Byte offset of the scale of block kb of weight row n in the MFMA-ordered layout:
-// each run of 16 blocks (four K steps of 128) is stored transposed, so that one
-// 32-bit word holds, for lane group g, the scales of four consecutive K steps.
+// Weight layouts in matrix-core order (rows counted across all matrices, N % 16 == 0):
+//  codes: each 16-row x 128-K tile (one K step of a 16-row MFMA block) is one
+//  contiguous kilobyte, tiles in (row block, K step) order; inside it row r's 64
+//  bytes, inside those block kb % 4's 16 bytes (element 2 i in the low nibble of
+//  byte i), so one wavefront's operand load for a block and K step reads one
+//  kilobyte;
+//  scales: each 16-row x 512-K group is 256 contiguous bytes, groups in (row
+//  block, four K steps) order; inside it row r's 16 bytes, holding the scales of
+//  the row's 16 blocks transposed 4 x 4 (byte 4 g + j = block 4 j + g), so one
+//  32-bit word gives lane group g the scales of four consecutive K steps.
+__device__ __host__ __forceinline__ int64_t wcode_offset(int64_t n, int kb, int K) {
+    return ((n / 16) * (K / kMxKStep) + kb / 4) * 1024 + (n % 16) * 64 + (kb % 4) * 16;
+}
 __device__ __host__ __forceinline__ int64_t wscale_offset(int64_t n, int kb, int K) {
-    return n * (K / kMxBlock) + (kb / 16) * 16 + (kb % 4) * 4 + (kb / 4) % 4;
+    return ((n / 16) * (K / (4 * kMxKStep)) + kb / 16) * 256 + (n % 16) * 16 + (kb % 4) * 4 + (kb / 4) % 4;
 }
 
-// One thread per block of 32 along K. kFp4: E2M1 codes packed two per byte and
-// scales in the MFMA order (weights); else E4M3 codes, one per byte, scales in
-// row order (activations).
+// One thread per block of 32 along K. kFp4: E2M1 codes packed two per byte, codes
+// and scales in matrix-core order (weights); else E4M3 codes, one per byte, codes
+// and scales in row order (activations).
 template <bool kFp4, class In>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__ in, int64_t rows, int K,
                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
@@ -108,7 +119,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__
             const uint32_t c = e2m1_mag(ldexpf(fabsf(v[i]), -s)) | (signbit(v[i]) ? 8u : 0u);
             w[i / 8] |= c << (4 * (i % 8));
         }
-        *reinterpret_cast<uint4*>(q + row * (K / 2) + kb * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(q + wcode_offset(row, kb, K)) = make_uint4(w[0], w[1], w[2], w[3]);
         scales[wscale_offset(row, kb, K)] = static_cast<uint8_t>(s + 127);
     } else {
         uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
@@ -134,7 +145,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__
 // down pass) and every row of the m-tile. Per K step of 128: the A rows (128
 // bytes each) and their four scale bytes are staged in LDS, double-buffered;
 // each lane loads its 16 bytes of E2M1 weights per block straight into
-// registers one step ahead, and one scale word per block every four steps.
+// registers (one kilobyte per wavefront, contiguous) three steps ahead, and one
+// scale word per block every four steps.
 
 constexpr int kMxWaves = 8;
 constexpr int kMxThreads = kMxWaves * 64;
@@ -142,7 +154,9 @@ constexpr int kMxNB = 2;
 constexpr int kMxKS = 128;
 constexpr int kMxMaxMB = 12;
 constexpr int kMxBM = 16 * kMxMaxMB;
-constexpr int kMxARow = kMxKS + 16;  // LDS bytes per staged row (padded)
+constexpr int kMxARow = kMxKS + 32;  // LDS bytes per staged row: 32 B of padding keeps the 16-byte
+                                     // fragment reads of 16 rows conflict-free (16 B measured 39 %
+                                     // of LDS-active cycles in bank conflicts)
 constexpr int kMxRowsPerPass = kMxThreads / (kMxKS / 16);
 static_assert(kMxBM % kMxRowsPerPass == 0, "whole staging passes");
 
@@ -205,11 +219,11 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
     uint32_t bs[2][kMxNB];     // weight scale words, two sets of four K steps
     auto load_b = [&](u32x4 (&dst)[kMxNB], int s) {
 #pragma unroll
-        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const u32x4*>(wq[b] + s * (kMxKS / 2));
+        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const u32x4*>(wq[b] + s * 1024);
     };
     auto load_bs = [&](uint32_t (&dst)[kMxNB], int q4) {
 #pragma unroll
-        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const uint32_t*>(wsc[b] + q4 * 16);
+        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const uint32_t*>(wsc[b] + q4 * 256);
     };
     // multiply one K step from LDS buffer `buf` with weights w and scale byte sel of words ws
     auto step = [&](int buf, const u32x4 (&w)[kMxNB], const uint32_t (&ws)[kMxNB], auto sel) {
@@ -342,8 +356,8 @@ void mx_grouped_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
         const uint8_t* q = kGated ? (b == 0 ? W0q : W1q) : W0q;
         const uint8_t* s = kGated ? (b == 0 ? W0s : W1s) : W0s;
         const int64_t n = wrows + n_safe + (kGated ? 0 : 16 * b) + fr;
-        wq[b] = q + n * (K / 2) + 16 * fg;
-        wsc[b] = s + wscale_offset(n, 0, K) + 4 * fg;
+        wq[b] = q + wcode_offset(n, 0, K) + 16 * fg;   // K step s: + s * 1024
+        wsc[b] = s + wscale_offset(n, 0, K) + 4 * fg;  // four K steps q4: + q4 * 256
     }
 
     const int mb = min(kMxMaxMB, (M + 31) / 32 * 2);

@@ -1,7 +1,8 @@
 """GPU parity of the MX-format expert path (MXFP4 weights, MXFP8 activations)
 against the CPU oracle, through the C ABI.
 
-  * codes and scales (weights, x rows, H rows): bit for bit. H's codes are
+  * codes and scales (weights, x rows, H rows): bit for bit (weights read back
+    from their matrix-core order as the header describes it). H's codes are
     compared with the oracle's quantisation of the device's own float32 H, so
     both sides decide on the same numbers;
   * H = silu(G) U from exact products accumulated in float32: with A_G, A_U
@@ -38,22 +39,32 @@ def moe(dev):
 
 
 def unpack_fp4(q):
-    """[..., K/2] bytes -> [..., K] codes, element 2i in the low nibble of byte i."""
-    q = gu.host(q).numpy().astype(np.int64)
+    """Row-major E2M1 codes [..., K/2] bytes -> [..., K] codes, element 2i in the low nibble of byte i."""
+    q = np.asarray(q, dtype=np.int64)
     out = np.empty(q.shape[:-1] + (2 * q.shape[-1],), dtype=np.int64)
     out[..., 0::2] = q & 0xF
     out[..., 1::2] = q >> 4
     return out
 
 
-def unswizzle_scales(sc):
-    """Weight scales [..., K/32] from the matrix-core order to row order: block kb of a
-    row sits at byte (kb // 16) * 16 + (kb % 4) * 4 + (kb // 4) % 4 of that row."""
+def weight_codes(q):
+    """MXFP4 weight codes in matrix-core order ([G, N, K/2] buffer: 16-row x 128-column
+    tiles of one kilobyte, 64 bytes per row) -> row-major codes [G, N, K]."""
+    q = gu.host(q).numpy()
+    G, N, K2 = q.shape
+    t = q.reshape(G, N // 16, K2 // 64, 16, 64).transpose(0, 1, 3, 2, 4).reshape(G, N, K2)
+    return unpack_fp4(t)
+
+
+def weight_scales(sc):
+    """MXFP4 weight scales in matrix-core order ([G, N, K/32] buffer: 16-row x 16-block
+    groups of 256 bytes, 16 bytes per row holding its blocks transposed 4 x 4) -> row order."""
     sc = gu.host(sc).numpy().astype(np.int64)
-    nb = sc.shape[-1]
+    G, N, nb = sc.shape
+    t = sc.reshape(G, N // 16, nb // 16, 16, 16).transpose(0, 1, 3, 2, 4).reshape(G, N, nb)
     kb = np.arange(nb)
     pos = (kb // 16) * 16 + (kb % 4) * 4 + (kb // 4) % 4
-    return sc[..., pos]
+    return t[..., pos]
 
 
 def _u8(t):
@@ -76,10 +87,10 @@ def test_mx_quantize_weights_bitexact(dev, moe, G, N, K):
     q, sc = moe.moe_mx_quantize_weights(w.to(dev))
     torch.cuda.synchronize()
     codes_ref, s_ref = mx.quantize(gu.f64(w), mx.E2M1)
-    codes = unpack_fp4(q)
+    codes = weight_codes(q)
     bad = np.argwhere(codes != codes_ref)
     assert bad.size == 0, f"E2M1 codes differ at {bad[:5].tolist()}"
-    assert np.array_equal(unswizzle_scales(sc), s_ref)
+    assert np.array_equal(weight_scales(sc), s_ref)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -107,7 +118,7 @@ def _mx_weights(moe, inp, dev):
 
 def _deq_w(pair, e):
     q, sc = pair
-    return mx.dequantize(unpack_fp4(q[e]), unswizzle_scales(sc[e]), mx.E2M1)
+    return mx.dequantize(weight_codes(q[e:e + 1])[0], weight_scales(sc[e:e + 1])[0], mx.E2M1)
 
 
 def _check_h(h_dev, X, Wg, Wu):
@@ -245,8 +256,8 @@ def test_mx_prefill_full_size_sampled(dev, moe):
                 src = {"gate": inp.w_gate, "up": inp.w_up, "down": inp.w_down}[name][e]
                 rows = r.choice(src.shape[0], size=8, replace=False)
                 cref, sref = mx.quantize(gu.f64(src[rows]), mx.E2M1)
-                assert np.array_equal(unpack_fp4(pair[0][e][rows]), cref), f"{name} codes of expert {e}"
-                assert np.array_equal(unswizzle_scales(pair[1][e][rows]), sref), f"{name} scales of expert {e}"
+                assert np.array_equal(weight_codes(pair[0][e:e + 1])[0][rows], cref), f"{name} codes of expert {e}"
+                assert np.array_equal(weight_scales(pair[1][e:e + 1])[0][rows], sref), f"{name} scales of expert {e}"
             _check_h(it("h_act")[row:row + 1], Xd[t:t + 1], _deq_w(wts[0], e), _deq_w(wts[1], e))
             hq, hs = it("h_q")[row:row + 1], it("h_s")[row:row + 1]
             Hd = mx.dequantize(_u8(hq), _u8(hs), mx.E4M3)
