@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--experts", choices=["bf16", "mxfp4"], default="bf16",
                     help="expert weight format: bf16, or MXFP4 weights with MXFP8 activations (weights quantised "
                          "once before the timed steps)")
+    ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed",
+                    help="bf16 expert weight layout: packed into 16 x 64 matrix-core tiles once before the timed "
+                         "steps (moe_pack_weights), or row-major [E, N, K]; both give the same output bit for bit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, run a plain float32 copy kernel (out = -in) over this many MiB three "
                          "times, so that a counter run can scale FETCH_SIZE / WRITE_SIZE by a known byte count")
@@ -62,9 +65,11 @@ def parse():
 class Layer:
     """Preallocated buffers and C-ABI calls for one workload."""
 
-    def __init__(self, lib, inp, cfg, dev):
+    def __init__(self, lib, inp, cfg, dev, weights=None, packed=False):
         import torch
         self.lib, self.inp, self.cfg, self.dev = lib, inp, cfg, dev
+        self.weights = weights if weights is not None else (inp.w_gate, inp.w_up, inp.w_down)
+        self.packed = packed
         T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
         n = T * k
         e = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
@@ -96,12 +101,15 @@ class Layer:
                         P(self.ws_perm), self.ws_perm.numel(), sp))
         if ev is not None:
             ev[0].record(self.stream)
-        c(L.moe_expert_gate_up(sh, P(i.x), P(self.row_src), P(self.offsets), P(i.w_gate), P(i.w_up), P(self.h_act),
-                               P(self.ws_ffn), self.ws_ffn.numel(), sp))
+        wg, wu, wd = self.weights
+        gate_up = L.moe_expert_gate_up_packed if self.packed else L.moe_expert_gate_up
+        down = L.moe_expert_down_packed if self.packed else L.moe_expert_down
+        c(gate_up(sh, P(i.x), P(self.row_src), P(self.offsets), P(wg), P(wu), P(self.h_act),
+                  P(self.ws_ffn), self.ws_ffn.numel(), sp))
         if ev is not None:
             ev[1].record(self.stream)
-        c(L.moe_expert_down(sh, P(self.h_act), P(self.offsets), P(i.w_down), P(self.y_rows), P(self.ws_ffn),
-                            self.ws_ffn.numel(), sp))
+        c(down(sh, P(self.h_act), P(self.offsets), P(wd), P(self.y_rows), P(self.ws_ffn),
+               self.ws_ffn.numel(), sp))
         if ev is not None:
             ev[2].record(self.stream)
         c(L.moe_combine(sh, P(self.y_rows), P(self.row_of), P(self.w), P(self.out), sp))
@@ -537,7 +545,7 @@ def main():
 
     from synthetic import CONFIGS, LATENT_CONFIGS, make_inputs
     from sparse_mixture_experts_fp32_amd import _lib as lib
-    from sparse_mixture_experts_fp32_amd import MoEForward
+    from sparse_mixture_experts_fp32_amd import MoEForward, moe_pack_weights
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -562,7 +570,13 @@ def main():
             result["cpu_baseline"] = mx_cpu_baseline(inp, cfg, min(args.cpu_experts, 4))
         print(json.dumps(result), flush=True)
         return
-    layer = Layer(lib, inp, cfg, dev)
+    packed = args.layout == "packed"
+    weights = None
+    if packed:  # once, before timing: the row-major tensors stay for the check and the CPU baseline
+        weights = tuple(moe_pack_weights(w) for w in (inp.w_gate, inp.w_up, inp.w_down))
+        torch.cuda.synchronize()
+        note("expert weights packed into matrix-core tiles")
+    layer = Layer(lib, inp, cfg, dev, weights, packed)
     note("buffers allocated")
 
     if args.copy_probe_mib > 0:
@@ -596,13 +610,13 @@ def main():
     gate_up_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     down_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
 
-    # the step is moe_forward's kernel sequence: same output, bit for bit
+    # the step is moe_forward's kernel sequence on row-major weights: same output, bit for bit
     fwd = MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
     ref_out = fwd(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down)
     torch.cuda.synchronize()
     assert torch.equal(ref_out, layer.out), "bench step and moe_forward disagree"
     del fwd, ref_out
-    note("bench step equals moe_forward bit for bit")
+    note("bench step equals moe_forward (row-major weights) bit for bit")
 
     T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
     n = T * k
@@ -632,7 +646,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} top-{k} h={h}, SwiGLU experts, fp32 gate",
-                   "T": T, "d": d, "E": E, "k": k, "h": h, "seed": cfg.seed,
+                   "T": T, "d": d, "E": E, "k": k, "h": h, "seed": cfg.seed, "weight_layout": args.layout,
                    "experts_touched": touched, "max_rows_per_expert": int(counts.max())},
         "gpu_ms_per_step": gpu_ms,
         "grouped_gemm": {"ms": gate_up_ms + down_ms, "tflops": gemm_tflops,

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -291,6 +291,31 @@ int moe_qb_histogram(const moe_shape_t* shape, const float* logits, const float*
                      float width, int32_t n_bins, int32_t* hist, void* stream);
 int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float width,
                   int32_t n_bins, const float* bias_in, float* bias_out, void* stream);
+
+/*
+ * ------------------------------------------------------------ packed weights
+ * Expert weights stored in matrix-core order: each 16-row x 64-column tile of a
+ * weight matrix [N, K] is 1024 contiguous elements (row r of the tile at element
+ * r * 64), tiles in (row block, column block) order, so one wavefront's operand
+ * loads of a 16-row block and a 64-deep K step read two contiguous kilobytes
+ * instead of 128 bytes from each of 16 rows. The values are the same; the
+ * *_packed calls give bitwise the results of their row-major counterparts.
+ *
+ * moe_pack_weights: w [groups, N, K] bf16 row-major (read) -> w_packed, the same
+ *  number of elements in packed order (written; must not overlap w). N a
+ *  multiple of 16, K of 64 (w_gate/w_up: N = h, K = d; w_down: N = d, K = h).
+ */
+int moe_pack_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint16_t* w_packed,
+                     void* stream);
+/* moe_expert_gate_up, moe_expert_down and moe_forward with packed expert weights. */
+int moe_expert_gate_up_packed(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                              const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                              uint16_t* h_act, void* ws, size_t ws_bytes, void* stream);
+int moe_expert_down_packed(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                           const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream);
+int moe_forward_packed(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
+                       const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
+                       const uint16_t* w_down, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ---------------------------------------------------------------- LatentMoE

@@ -384,9 +384,9 @@ int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* a, const int32_t* a
     return hip_status(err, "down launch");
 }
 
-int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
-                       const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
-                       void* ws, size_t ws_bytes, void* stream) {
+static int expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                          const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                          uint16_t* h_act, void* ws, size_t ws_bytes, void* stream, bool packed) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -404,12 +404,24 @@ int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_
     hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
     err = moe::launch_gate_up(a, a_rows, shape->T, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h,
-                              w_gate, w_up, h_act, s);
+                              w_gate, w_up, h_act, s, packed);
     return hip_status(err, "gate_up launch");
 }
 
-int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
-                    const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                       const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
+                       void* ws, size_t ws_bytes, void* stream) {
+    return expert_gate_up(shape, a, a_rows, expert_offsets, w_gate, w_up, h_act, ws, ws_bytes, stream, false);
+}
+
+int moe_expert_gate_up_packed(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                              const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                              uint16_t* h_act, void* ws, size_t ws_bytes, void* stream) {
+    return expert_gate_up(shape, a, a_rows, expert_offsets, w_gate, w_up, h_act, ws, ws_bytes, stream, true);
+}
+
+static int expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                       const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream, bool packed) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -424,8 +436,31 @@ int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32
     const FfnWs fw = ffn_carve(shape, ws);
     hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s,
+                           packed);
     return hip_status(err, "down launch");
+}
+
+int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                    const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    return expert_down(shape, h_act, expert_offsets, w_down, y_rows, ws, ws_bytes, stream, false);
+}
+
+int moe_expert_down_packed(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                           const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
+    return expert_down(shape, h_act, expert_offsets, w_down, y_rows, ws, ws_bytes, stream, true);
+}
+
+int moe_pack_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint16_t* w_packed, void* stream) {
+    if (groups < 0 || N < 0 || N % 16 != 0 || K < 64 || K % 64 != 0 || K > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "bad weight shape (groups %lld, N %d, K %d; N a multiple of 16, K of 64)",
+                    static_cast<long long>(groups), N, K);
+    if (groups == 0 || N == 0) return ok();
+    MOE_CHECK_PTR(w);
+    MOE_CHECK_PTR(w_packed);
+    if (w == w_packed) return fail(MOE_ERR_INVALID_ARG, "w_packed must not be w (no packing in place)");
+    hipError_t err = moe::launch_pack_weights(w, groups * N, K, w_packed, static_cast<hipStream_t>(stream));
+    return hip_status(err, "pack_weights launch");
 }
 
 int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* row_of, const float* topk_w,
@@ -502,9 +537,9 @@ int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float
     return hip_status(err, "qb_update launch");
 }
 
-int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
-                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
-                size_t ws_bytes, void* stream) {
+static int forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
+                   size_t ws_bytes, void* stream, bool packed) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -546,12 +581,24 @@ int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_rout
     if (err != hipSuccess) return hip_status(err, "permute launch");
     err = moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x, row_src, T, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s);
+    err = moe::launch_gate_up(x, row_src, T, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s, packed);
     if (err != hipSuccess) return hip_status(err, "gate_up launch");
-    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, d, E, h, w_down, y_rows, s);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, d, E, h, w_down, y_rows, s, packed);
     if (err != hipSuccess) return hip_status(err, "down launch");
     err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
     return hip_status(err, "combine launch");
+}
+
+int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
+                size_t ws_bytes, void* stream) {
+    return forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, out, ws, ws_bytes, stream, false);
+}
+
+int moe_forward_packed(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+                       const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
+                       size_t ws_bytes, void* stream) {
+    return forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, out, ws, ws_bytes, stream, true);
 }
 
 size_t moe_latent_workspace_bytes(const moe_latent_shape_t* shape) {

@@ -164,10 +164,24 @@ def moe_combine(y_rows, row_of, topk_w):
     return out
 
 
-class MoEForward:
-    """moe_forward with a reusable workspace (allocated once per shape)."""
+def moe_pack_weights(w):
+    """Expert weights w [G, N, K] bf16 in matrix-core order (16-row x 64-column tiles of
+    1024 contiguous elements): the same values, a new tensor of the same shape whose
+    memory is in packed order (for MoEForward(..., packed=True) and the *_packed calls)."""
+    _need(w, "w", "bf16")
+    dev = w.device
+    G, N, K = w.shape
+    out = torch.empty_like(w)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_pack_weights(G, N, K, _ptr(w), _ptr(out), _stream(dev)))
+    return out
 
-    def __init__(self, T: int, d: int, E: int, k: int, h: int, device):
+
+class MoEForward:
+    """moe_forward (moe_forward_packed when packed) with a reusable workspace."""
+
+    def __init__(self, T: int, d: int, E: int, k: int, h: int, device, packed: bool = False):
+        self.packed = packed
         self.shape = _lib.shape(T, d, E, k, h)
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
         self.device = torch.device(device)
@@ -185,10 +199,10 @@ class MoEForward:
         if out is None:
             out = torch.empty((T, d), dtype=torch.float32, device=dev)
         _need(out, "out", "f32", (T, d), dev)
+        fn = _lib.lib.moe_forward_packed if self.packed else _lib.lib.moe_forward
         with torch.cuda.device(dev):
-            _lib.check(_lib.lib.moe_forward(ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias),
-                                            _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(self.ws),
-                                            self.ws.numel(), _stream(dev)))
+            _lib.check(fn(ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate),
+                          _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(self.ws), self.ws.numel(), _stream(dev)))
         return out
 
     def intermediate(self, name: str) -> torch.Tensor:

@@ -1,0 +1,82 @@
+"""GPU tests of the packed expert-weight layout: packing moves every element to
+the place include/moe.h states (bit for bit), and every *_packed call gives
+bitwise the result of its row-major counterpart (the same products in the same
+order), from tiny layers to the full prefill layer."""
+import numpy as np
+import pytest
+import torch
+
+from synthetic import CONFIGS, make_inputs, scaled_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_mixture_experts_fp32_amd  # noqa: F401  (fails loudly if libmoe.so is missing)
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def moe(dev):
+    import sparse_mixture_experts_fp32_amd as m
+    return m
+
+
+def _unpack(p):
+    """Packed [G, N, K] -> row-major: tile (n // 16, k // 64) is 1024 contiguous elements,
+    row r of it at r * 64."""
+    G, N, K = p.shape
+    flat = p.reshape(G, N // 16, K // 64, 16, 64)
+    return flat.permute(0, 1, 3, 2, 4).reshape(G, N, K)
+
+
+@pytest.mark.parametrize("G,N,K", [(3, 32, 128), (2, 48, 512), (1, 2048, 7168)])
+def test_pack_weights_layout(dev, moe, G, N, K):
+    g = torch.Generator(device="cpu").manual_seed(G * N + K)
+    w = torch.randn((G, N, K), generator=g).to(torch.bfloat16).to(dev)
+    p = moe.moe_pack_weights(w)
+    torch.cuda.synchronize()
+    assert torch.equal(_unpack(p.view(torch.int16)).view(torch.bfloat16), w)
+
+
+CASES = {
+    "tiny": dict(),
+    "ragged": dict(T=77, d=256, E=12, k=3, h=384),
+    "many_tiles": dict(T=1000, d=128, E=3, k=2, h=256),
+    "one_token": dict(T=1, E=5, k=2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_forward_packed_equals_rowmajor(dev, moe, case):
+    cfg = scaled_config("tiny", name=f"packed_{case}", **CASES[case])
+    di = make_inputs(cfg).to(dev)
+    ref = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)(di.x, di.w_router, di.router_bias, di.w_gate,
+                                                                di.w_up, di.w_down)
+    pw = [moe.moe_pack_weights(w) for w in (di.w_gate, di.w_up, di.w_down)]
+    fwd = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev, packed=True)
+    out = fwd(di.x, di.w_router, di.router_bias, *pw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.slow
+def test_forward_packed_equals_rowmajor_prefill(dev, moe):
+    cfg = CONFIGS["prefill"]
+    print("packed prefill: drawing inputs", flush=True)
+    inp = make_inputs(cfg, device=dev)
+    ref = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)(inp.x, inp.w_router, None, inp.w_gate, inp.w_up,
+                                                                inp.w_down)
+    torch.cuda.synchronize()
+    ref = ref.clone()
+    packed = []
+    for name in ("w_gate", "w_up", "w_down"):  # one tensor at a time, freeing the row-major one
+        w = getattr(inp, name)
+        packed.append(moe.moe_pack_weights(w))
+        setattr(inp, name, None)
+        del w
+    out = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev, packed=True)(inp.x, inp.w_router, None, *packed)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
