@@ -515,14 +515,17 @@ def mx_cpu_baseline(inp, cfg, n_experts):
                        f"{scale:.0f}; {sum(t.values()):.1f} s measured, {layer_s:.0f} s estimated per layer")}
 
 
-def measured_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter record, or None if the kernel changed since."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per gate/up launch from the committed counter record, or None if the record is for
+    another kernel or the kernel's sources changed since."""
     import hashlib
     path = TRAFFIC_RECORD.format(workload=workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if kernel not in rec["kernel"]:
+        return None
     h = hashlib.sha256()
     for src in rec["sources"]:
         p = os.path.join(ROOT, src)
@@ -632,6 +635,9 @@ def main():
     down_bytes = 2.0 * n * h + 2.0 * d * h * touched + 4.0 * n * d
     down_gbs = down_bytes / (down_ms * 1e-3) / 1e9
     ms = wall_ms
+    # the gate/up kernel: the LDS-ring kernel on packed weights, the register-streaming one on row-major
+    gu_kernel = ("ffn_ring_kernel<true, true> (gate/up pass + SwiGLU, packed weights)" if packed else
+                 "grouped_ffn_kernel<moe::GemmCfg<1, 8, 2, 64, 12, true, 16>, true, false> (gate/up pass + SwiGLU)")
     result = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -653,9 +659,9 @@ def main():
                          "mfma_frac": gemm_tflops / MFMA_BF16_PEAK_TFLOPS,
                          "gate_up_ms": gate_up_ms, "down_ms": down_ms,
                          "down_gbs": down_gbs, "down_hbm_frac": down_gbs / HBM_PEAK_GBS},
-        "roofline": {"kernel": "grouped_ffn_kernel<gated> (gate/up pass + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": gu_kernel, "bound": "hbm",
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(cfg.name), "algorithmic_bytes": gu_bytes},
+                     "traffic": measured_traffic(cfg.name, gu_kernel.split(" ")[0]), "algorithmic_bytes": gu_bytes},
     }
     result["balance"] = Balance(layer).measure(max(K, 10))
     note("load-balancing calls timed")

@@ -294,16 +294,18 @@ int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float
 
 /*
  * ------------------------------------------------------------ packed weights
- * Expert weights stored in matrix-core order: each 16-row x 64-column tile of a
- * weight matrix [N, K] is 1024 contiguous elements (row r of the tile at element
- * r * 64), tiles in (row block, column block) order, so one wavefront's operand
- * loads of a 16-row block and a 64-deep K step read two contiguous kilobytes
- * instead of 128 bytes from each of 16 rows. The values are the same; the
- * *_packed calls give bitwise the results of their row-major counterparts.
+ * Expert weights stored in matrix-core fragment order: a weight matrix [N, K] is
+ * cut into tiles of 16 rows x 32 columns, 512 contiguous elements each, in
+ * (row block, column block) order; inside a tile, element (r, c) sits at
+ * (r + 16 * (c / 8)) * 8 + c % 8, which is the order in which the 64 lanes of a
+ * wavefront hold one 16 x 32 MFMA operand (lane l: row l % 16, columns
+ * 8 * (l / 16) .. + 7). One kilobyte of HBM then is one operand, loaded in one
+ * contiguous run straight into LDS. The values are the same; the *_packed calls
+ * give bitwise the results of their row-major counterparts.
  *
  * moe_pack_weights: w [groups, N, K] bf16 row-major (read) -> w_packed, the same
  *  number of elements in packed order (written; must not overlap w). N a
- *  multiple of 16, K of 64 (w_gate/w_up: N = h, K = d; w_down: N = d, K = h).
+ *  multiple of 16, K of 32 (w_gate/w_up: N = h, K = d; w_down: N = d, K = h).
  */
 int moe_pack_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint16_t* w_packed,
                      void* stream);

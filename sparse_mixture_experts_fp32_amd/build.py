@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "balance.hip", "latent.hip", "mx.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "ffn_ring.hip", "combine.hip", "balance.hip", "latent.hip", "mx.hip", "moe_api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

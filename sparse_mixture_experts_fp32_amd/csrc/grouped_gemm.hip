@@ -163,7 +163,7 @@ __device__ __forceinline__ void mfma_step(f32x4 (&acc)[kNB][kMBW], const uint16_
 // Every load and LDS store in the K loop is unconditional: rows past M re-read
 // row M - 1 and prefetch indices are clamped to the last K step (a repeated
 // step is loaded but never used).
-template <class C, bool kGated, bool kBf16, bool kPacked, int kMB>
+template <class C, bool kGated, bool kBf16, int kMB>
 __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restrict__ A,
                                          const int32_t* __restrict__ A_rows, int64_t A_nrows, int64_t row0, int M,
                                          const uint16_t* const (&wb)[C::kNB], bool wave_on, int N, int K, int wm,
@@ -201,10 +201,6 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
         for (int i = 0; i < kMBW; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / kKS;
-    // weight K offset of a step: row-major rows advance by the K step, packed tiles
-    // (16 rows x 64 columns, 1024 elements each) by one tile per 64 columns
-    constexpr int kWMul = kPacked ? 16 : 1;
-    static_assert(!kPacked || kKS == 64, "packed weights are tiled for 64-deep K steps");
     if constexpr (!C::kDeep) {
         // Weights and A rows one K step ahead: register sets b0 / b1 and LDS
         // buffers 0 / 1 alternate between "being consumed" and "being filled".
@@ -217,13 +213,13 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
         for (int s0 = 0; s0 < nk; s0 += 2) {
             const int k1 = min(s0 + 1, nk - 1) * kKS;
             load_rows(a_reg, a_src, a_off, k1);
-            load_weights(b1, wb, k1 * kWMul);
+            load_weights(b1, wb, k1);
             if (wave_on) mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[0], b0);
             store_rows<kAPasses, kPassStride>(a_dst[1], a_reg);
             __syncthreads();
             const int k2 = min(s0 + 2, nk - 1) * kKS;
             load_rows(a_reg, a_src, a_off, k2);
-            load_weights(b0, wb, k2 * kWMul);
+            load_weights(b0, wb, k2);
             if (wave_on && s0 + 1 < nk) mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[1], b1);
             store_rows<kAPasses, kPassStride>(a_dst[0], a_reg);
             __syncthreads();
@@ -241,15 +237,15 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
         load_rows(ar[0], a_src, a_off, 0);
         load_rows(ar[1], a_src, a_off, min(1, nk - 1) * kKS);
         load_weights(bw[0], wb, 0);
-        load_weights(bw[1], wb, min(1, nk - 1) * kKS * kWMul);
-        load_weights(bw[2], wb, min(2, nk - 1) * kKS * kWMul);
+        load_weights(bw[1], wb, min(1, nk - 1) * kKS);
+        load_weights(bw[2], wb, min(2, nk - 1) * kKS);
         store_rows<kAPasses, kPassStride>(a_dst[0], ar[0]);
         __syncthreads();
 #define MOE_DEEP_STEP(U)                                                                                  \
     {                                                                                                     \
         const int step = s0 + (U);                                                                        \
         load_rows(ar[(U) % 2], a_src, a_off, min(step + 2, nk - 1) * kKS);                                \
-        load_weights(bw[((U) + 3) % 4], wb, min(step + 3, nk - 1) * kKS * kWMul);                         \
+        load_weights(bw[((U) + 3) % 4], wb, min(step + 3, nk - 1) * kKS);                                 \
         if (wave_on && step < nk)                                                                         \
             mfma_step<kMBW, C::kWM, kNB, kSub, C::kAStride>(acc, a_frag[(U) % 2], bw[(U) % 4]);            \
         store_rows<kAPasses, kPassStride>(a_dst[((U) + 1) % 2], ar[((U) + 1) % 2]);                       \
@@ -294,7 +290,7 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
 // One workgroup per CU is the design point (LDS tile and register budget), so the
 // register allocator is told that occupancy is fixed and may spend registers on
 // keeping loads in flight rather than on reaching a higher wave count.
-template <class C, bool kGated, bool kBf16, bool kPacked>
+template <class C, bool kGated, bool kBf16>
 __global__ __launch_bounds__(C::kThreads) __attribute__((amdgpu_waves_per_eu(1, C::kWaves / 4)))
 void grouped_ffn_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ A_rows, int64_t A_nrows,
@@ -332,10 +328,7 @@ void grouped_ffn_kernel(
     // weight rows of this lane for the four B blocks (an idle wave reads valid rows it never uses)
     const int n_safe = wave_on ? n_wave : 0;
     const int64_t wexp = static_cast<int64_t>(e) * N * K;
-    // row-major: row n at n * K; packed: the 16-row tile of rows n_safe .. n_safe + 15
-    // starts at n_safe * K and row r of it at r * 64 (columns advance by whole tiles)
-    const int64_t lane_off = static_cast<int64_t>(n_safe) * K + static_cast<int64_t>(frag_row) * (kPacked ? 64 : K) +
-                             frag_k;
+    const int64_t lane_off = static_cast<int64_t>(n_safe + frag_row) * K + frag_k;
     const uint16_t* w0 = W0 + wexp + lane_off;
     const uint16_t* w1 = kGated ? W1 + wexp + lane_off : w0;
     const int64_t blk = 16 * static_cast<int64_t>(K);
@@ -350,7 +343,7 @@ void grouped_ffn_kernel(
     const int mb = min(C::kMaxMB, ((M + 16 * kStepMB - 1) / (16 * kStepMB)) * kStepMB);
 #define MOE_TILE(NB)                                                                                   \
     if (mb == (NB)) {                                                                                  \
-        ffn_tile<C, kGated, kBf16, kPacked, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, A_rows, A_nrows, row0, M, \
+        ffn_tile<C, kGated, kBf16, ((NB) < C::kMaxMB ? (NB) : C::kMaxMB)>(sA, A, A_rows, A_nrows, row0, M,          \
                                                                           wb, wave_on, N, K, wm, n_wave, Cout); \
         return;                                                                                        \
     }
@@ -374,7 +367,7 @@ static int max_tiles_for(int64_t n_rows, int E, int bm) {
     return static_cast<int>(t);
 }
 
-template <class C, bool kGated, bool kBf16 = false, bool kPacked = false>
+template <class C, bool kGated, bool kBf16 = false>
 hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows, const int4* tiles,
                       const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* W0, const uint16_t* W1, int N,
                       int K, void* Cout, hipStream_t stream) {
@@ -384,8 +377,7 @@ hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows,
     const int n_tiles = (N + cols_wg - 1) / cols_wg;
     const int slots = (max_tiles_for(n_rows, E, C::kBM) + kXcds - 1) / kXcds;
     const int64_t grid = static_cast<int64_t>(kXcds) * slots * n_tiles;
-    hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated, kBf16, kPacked>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0,
-                       stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
+    hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated, kBf16>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
     return hipGetLastError();
 }
 
@@ -415,41 +407,17 @@ hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nr
                           const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,
                           const uint16_t* w_up, uint16_t* h_act, hipStream_t stream, bool packed) {
     if (packed)
-        return launch_ffn<GateUpCfg, true, false, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate,
-                                                        w_up, h, d, h_act, stream);
+        return launch_gate_up_ring(a, a_rows, a_nrows, tiles, tile_start, n_rows, d, E, h, w_gate, w_up, h_act, true,
+                                   stream);
     return launch_ffn<GateUpCfg, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act,
                                        stream);
 }
 
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream, bool packed) {
-    if (packed)
-        return launch_ffn<DownCfg, false, false, true>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down,
-                                                       nullptr, d, h, y_rows, stream);
+    if (packed) return launch_down_ring(h_act, tiles, tile_start, n_rows, d, E, h, w_down, y_rows, true, stream);
     return launch_ffn<DownCfg, false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
                                       y_rows, stream);
-}
-
-// Row-major [groups * N, K] bf16 -> 16-row x 64-column tiles of 1024 contiguous
-// elements in (row block, column block) order, row r of a tile at element r * 64.
-// One thread per 8 elements (16 bytes).
-__global__ __launch_bounds__(256) void pack_weights_kernel(const uint16_t* __restrict__ w, int64_t rows, int K,
-                                                           uint16_t* __restrict__ out) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;  // 8-element chunk
-    const int64_t per_row = K / 8;
-    if (i >= rows * per_row) return;
-    const int64_t n = i / per_row;
-    const int k = static_cast<int>(i % per_row) * 8;
-    const int64_t dst = ((n / 16) * (K / 64) + k / 64) * 1024 + (n % 16) * 64 + (k % 64);
-    *reinterpret_cast<u32x4*>(out + dst) = *reinterpret_cast<const u32x4*>(w + n * K + k);
-}
-
-hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int K, uint16_t* out, hipStream_t stream) {
-    const int64_t n = rows * (K / 8);
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(pack_weights_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, w,
-                       rows, K, out);
-    return hipGetLastError();
 }
 
 hipError_t launch_dense(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,

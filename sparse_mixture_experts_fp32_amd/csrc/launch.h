@@ -29,8 +29,16 @@ hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nr
                           const uint16_t* w_up, uint16_t* h_act, hipStream_t stream, bool packed = false);
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream, bool packed = false);
-// row-major bf16 [rows, K] (rows % 16 == 0, K % 64 == 0) -> packed 16 x 64 tiles
+// row-major bf16 [rows, K] (rows % 16 == 0, K % 32 == 0) -> packed 16 x 32 fragment-order tiles
 hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int K, uint16_t* out, hipStream_t stream);
+// the expert passes on the LDS-ring kernel (packed or row-major weights; same tile list and results)
+hipError_t launch_gate_up_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                               const int32_t* tile_start, int64_t n_rows, int d, int E, int h,
+                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, bool packed,
+                               hipStream_t stream);
+hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
+                            int d, int E, int h, const uint16_t* w_down, float* y_rows, bool packed,
+                            hipStream_t stream);
 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T,
                           int d, int k, int64_t n_rows, float* out, hipStream_t stream);

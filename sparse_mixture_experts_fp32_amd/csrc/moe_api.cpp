@@ -452,13 +452,16 @@ int moe_expert_down_packed(const moe_shape_t* shape, const uint16_t* h_act, cons
 }
 
 int moe_pack_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint16_t* w_packed, void* stream) {
-    if (groups < 0 || N < 0 || N % 16 != 0 || K < 64 || K % 64 != 0 || K > (1 << 20))
-        return fail(MOE_ERR_INVALID_ARG, "bad weight shape (groups %lld, N %d, K %d; N a multiple of 16, K of 64)",
+    if (groups < 0 || N < 0 || N % 16 != 0 || K < 32 || K % 32 != 0 || K > (1 << 20))
+        return fail(MOE_ERR_INVALID_ARG, "bad weight shape (groups %lld, N %d, K %d; N a multiple of 16, K of 32)",
                     static_cast<long long>(groups), N, K);
     if (groups == 0 || N == 0) return ok();
     MOE_CHECK_PTR(w);
     MOE_CHECK_PTR(w_packed);
-    if (w == w_packed) return fail(MOE_ERR_INVALID_ARG, "w_packed must not be w (no packing in place)");
+    const uintptr_t bytes = static_cast<uintptr_t>(groups) * static_cast<uintptr_t>(N) * static_cast<uintptr_t>(K) * 2u;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(w_packed);
+    if (a < b + bytes && b < a + bytes)
+        return fail(MOE_ERR_INVALID_ARG, "w_packed overlaps w (no packing in place)");
     hipError_t err = moe::launch_pack_weights(w, groups * N, K, w_packed, static_cast<hipStream_t>(stream));
     return hip_status(err, "pack_weights launch");
 }

@@ -276,8 +276,9 @@ def test_packed_calls_check_arguments(lib):
     L = lib.lib
     a, b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     assert L.moe_pack_weights(2, 24, 128, a, b, None) == 1     # N not a multiple of 16
-    assert L.moe_pack_weights(2, 32, 96, a, b, None) == 1      # K not a multiple of 64
+    assert L.moe_pack_weights(2, 32, 80, a, b, None) == 1      # K not a multiple of 32
     assert L.moe_pack_weights(2, 32, 128, a, a, None) == 1     # in place
+    assert L.moe_pack_weights(2, 32, 128, a, ctypes.c_void_p(4096 + 2 * 32 * 128 * 2 - 16), None) == 1  # overlap
     assert L.moe_pack_weights(2, 32, 128, None, b, None) == 1
     assert L.moe_pack_weights(0, 32, 128, None, None, None) == 0
     s = _shape(lib)

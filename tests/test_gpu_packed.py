@@ -25,14 +25,14 @@ def moe(dev):
 
 
 def _unpack(p):
-    """Packed [G, N, K] -> row-major: tile (n // 16, k // 64) is 1024 contiguous elements,
-    row r of it at r * 64."""
+    """Packed [G, N, K] -> row-major: tile (n // 16, k // 32) is 512 contiguous elements,
+    element (r, c) of it at (r + 16 * (c // 8)) * 8 + c % 8."""
     G, N, K = p.shape
-    flat = p.reshape(G, N // 16, K // 64, 16, 64)
-    return flat.permute(0, 1, 3, 2, 4).reshape(G, N, K)
+    t = p.reshape(G, N // 16, K // 32, 4, 16, 8)  # (.., column group c // 8, row r, c % 8)
+    return t.permute(0, 1, 4, 2, 3, 5).reshape(G, N, K)
 
 
-@pytest.mark.parametrize("G,N,K", [(3, 32, 128), (2, 48, 512), (1, 2048, 7168)])
+@pytest.mark.parametrize("G,N,K", [(3, 32, 128), (2, 48, 96), (1, 2048, 7168)])
 def test_pack_weights_layout(dev, moe, G, N, K):
     g = torch.Generator(device="cpu").manual_seed(G * N + K)
     w = torch.randn((G, N, K), generator=g).to(torch.bfloat16).to(dev)
