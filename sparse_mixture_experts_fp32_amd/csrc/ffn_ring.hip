@@ -38,6 +38,7 @@
 // tile element (r, c) sits at ((r + 16 (c / 8)) * 8 + c % 8).
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -52,43 +53,6 @@ constexpr int kRAStage = kRMaxMB * 1024;             // bytes of A rows per stag
 constexpr int kRWStage = kRWaves * kRNB * 1024;      // bytes of weight rows per stage
 constexpr int kRStage = kRAStage + kRWStage;         // 44 KiB
 constexpr int kRFragAhead = 4;                       // A fragments read ahead of their MFMAs
-
-// One 1 KiB direct-to-LDS load: lane l copies 16 bytes from sbase + voff to LDS
-// byte lds + 16 l (lds is wave-uniform). M0 carries the LDS address; nothing
-// else in these kernels uses M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-static __device__ __forceinline__ void dma_saddr(uint32_t lds, const void* sbase, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
-}
-static __device__ __forceinline__ void dma_vaddr(uint32_t lds, const void* addr) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Wait until at most N of this wave's loads are in flight and its LDS reads are
-// done, then barrier.
-template <int N>
-static __device__ __forceinline__ void wait_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-static __device__ __forceinline__ void wait_loads_barrier(int n) {  // n wave-uniform, 0 .. 2
-    switch (n) {
-        case 0: wait_barrier<0>(); break;
-        case 1: wait_barrier<1>(); break;
-        default: wait_barrier<2>(); break;
-    }
-}
-
-static __device__ __forceinline__ const void* uniform_ptr(const void* p) {
-    const uint64_t v = reinterpret_cast<uint64_t>(p);
-    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
-    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 // acc[j][i] += A block i (from LDS) x weight block j (from LDS), one K step.
 template <int kMB>
@@ -125,7 +89,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar branches below
     const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
-    const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(ring));
+    const uint32_t ring_lds = lds_addr(ring);
 
     // A blocks this wave loads: wave and wave + 8 (when below kMB); lane l reads
     // row 16 blk + l % 16 (clamped to the tile, gathered through A_rows), K 8 (l / 16) ...
@@ -257,17 +221,23 @@ void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__
         wblk[b] = static_cast<const uint16_t*>(uniform_ptr(base + wexp + off));
     }
 
-    const int mb = min(kRMaxMB, (M + 31) / 32 * 2);
+    const int mb = min(kRMaxMB, (M + 15) / 16);
 #define MOE_RING_TILE(NB)                                                                                  \
     if (mb == (NB)) {                                                                                      \
         ring_tile<kGated, kPacked, (NB)>(ring, A, A_rows, A_nrows, row0, M, wblk, wave_on, N, K, n_out, Cout); \
         return;                                                                                            \
     }
+    MOE_RING_TILE(1)
     MOE_RING_TILE(2)
+    MOE_RING_TILE(3)
     MOE_RING_TILE(4)
+    MOE_RING_TILE(5)
     MOE_RING_TILE(6)
+    MOE_RING_TILE(7)
     MOE_RING_TILE(8)
+    MOE_RING_TILE(9)
     MOE_RING_TILE(10)
+    MOE_RING_TILE(11)
     MOE_RING_TILE(12)
 #undef MOE_RING_TILE
 }

@@ -6,9 +6,9 @@
 
 namespace moe {
 
-size_t router_parts_bytes(int d, int E);  // workspace of launch_router_gemm: 3 bf16 parts of w
-hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits,
-                              int64_t T, int d, int E, uint16_t* parts, hipStream_t stream);
+size_t router_ws_bytes(int64_t T, int d, int E);  // workspace of launch_router_gemm (weight parts, partial sums)
+hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits, int64_t T, int d,
+                              int E, void* ws, hipStream_t stream);
 hipError_t launch_topk_softmax(const float* logits, int64_t T, int E, int k, int32_t* topk_idx,
                                float* topk_w, hipStream_t stream);
 

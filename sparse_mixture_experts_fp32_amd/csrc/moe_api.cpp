@@ -81,7 +81,7 @@ size_t permute_ws(const moe_shape_t* s) {
 
 size_t route_ws(const moe_shape_t* s) {
     if (s->T == 0) return 0;
-    return align_up(moe::router_parts_bytes(s->d, s->E));
+    return align_up(moe::router_ws_bytes(s->T, s->d, s->E));
 }
 
 // The grouped GEMM's workspace: the m-tile list, then each expert's first m-tile index.

@@ -5,6 +5,7 @@
 // Frontier", section "Mixture-of-Experts with Dynamic Load Balancing".
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 #include "select.h"
 
 #include <algorithm>
@@ -21,125 +22,197 @@ namespace moe {
 // router_split_kernel. Each product x * part is exact in float32 because both
 // factors carry at most 8 significant bits, and the three products accumulate
 // in the MFMA's float32 accumulator: a float32 accumulation of exact products
-// on the bf16 matrix cores.
+// on the bf16 matrix cores. Per 32-deep K step and output block the order is
+// lo, mid, hi.
 //
-// Tile: 64 tokens x 64 experts per 256-thread workgroup, K step 64, the token
-// rows and the three weight parts staged in LDS (double-buffered); wave
-// (wm, wn) owns a 32 x 32 quarter as 2 x 2 blocks of 16 x 16.
+// The parts are written in MFMA fragment order (16 experts x 32 K per
+// kilobyte, lane l's 16 bytes = expert l % 16, K 8 (l / 16) .. + 7), the expert
+// count padded to a multiple of 16 with zero rows, so that one direct-to-LDS
+// load brings one operand.
+//
+// router_gemm_kernel: 256 tokens x 128 experts per 512-thread workgroup; wave
+// (wm, wn) owns 64 tokens x 64 experts (16 accumulator blocks, each fed by the
+// three parts), so every fragment read from LDS feeds 4 or 12 MFMAs. x rows and
+// weight parts go straight into a 3-stage LDS ring. The traffic of such a GEMM
+// is x once per expert block plus the weights once per token block, so the
+// tile is tall in tokens (the three parts weigh three x rows). K is split into
+// S ranges when the token x expert tiles alone would leave CUs idle (a
+// decode-sized batch has one token block): each range writes a float32 partial
+// sum and router_reduce_kernel adds the S partials in range order (and the
+// bias), so the result does not depend on scheduling. The workgroups of one
+// (token block, K range) are dealt to one XCD back to back, so its x rows come
+// from HBM once.
 
-constexpr int kRBM = 64, kRBN = 64, kRBK = 64;
-constexpr int kRStride = kRBK + 16;  // bf16 per LDS row (32 B of padding: conflict-free 16-B reads)
+constexpr int kRtBM = 256, kRtBN = 128, kRtKS = 32, kRtStages = 3;
+constexpr int kRtAStage = (kRtBM / 16) * 1024;        // 16 KiB of x rows per stage
+constexpr int kRtBStage = 3 * (kRtBN / 16) * 1024;    // 24 KiB of weight parts per stage
+constexpr int kRtStage = kRtAStage + kRtBStage;       // 40 KiB
+constexpr int kRtLoads = kRtStage / 1024 / 8;         // loads per wave per stage (5)
 
-// w [E, d] float32 -> parts [3][E][d] bf16 with w = parts[0] + parts[1] + parts[2] exactly.
-__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w, int64_t n,
+static __host__ __device__ int router_epad(int E) { return (E + 15) / 16 * 16; }
+
+// w [E, d] float32 -> parts [3][Epad x d] bf16 in fragment order, w = parts[0] + parts[1] + parts[2]
+// exactly; rows E .. Epad - 1 are zero. One thread per 16 bytes of each part, in destination order
+// (a wavefront writes one contiguous kilobyte; its lane l reads 8 consecutive K of expert l % 16).
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w, int E, int epad, int d,
                                                            uint16_t* __restrict__ parts) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-        const float v = w[i];
-        const uint16_t h = f32_to_bf16_bits(v);
-        const float r1 = v - bf16_bits_to_f32(h);
-        const uint16_t m = f32_to_bf16_bits(r1);
-        const float r2 = r1 - bf16_bits_to_f32(m);
-        parts[i] = h;
-        parts[n + i] = m;
-        parts[2 * n + i] = f32_to_bf16_bits(r2);
+    const int64_t chunks = static_cast<int64_t>(epad) * (d / 8);
+    const int64_t pn = static_cast<int64_t>(epad) * d;  // elements per part
+    const int ktiles = d / 32;
+    for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < chunks;
+         c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t tile = c / 64;
+        const int l = static_cast<int>(c % 64);
+        const int e = static_cast<int>(tile / ktiles) * 16 + l % 16;
+        const int k = static_cast<int>(tile % ktiles) * 32 + 8 * (l / 16);
+        float v[8];
+        if (e < E) {
+            const float4 lo = *reinterpret_cast<const float4*>(w + static_cast<int64_t>(e) * d + k);
+            const float4 hi = *reinterpret_cast<const float4*>(w + static_cast<int64_t>(e) * d + k + 4);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w; v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        }
+        uint16_t h[8], m[8], lo16[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            h[i] = f32_to_bf16_bits(v[i]);
+            const float r1 = v[i] - bf16_bits_to_f32(h[i]);
+            m[i] = f32_to_bf16_bits(r1);
+            lo16[i] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m[i]));
+        }
+        u32x4 vh, vm, vl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            vh[i] = h[2 * i] | (static_cast<uint32_t>(h[2 * i + 1]) << 16);
+            vm[i] = m[2 * i] | (static_cast<uint32_t>(m[2 * i + 1]) << 16);
+            vl[i] = lo16[2 * i] | (static_cast<uint32_t>(lo16[2 * i + 1]) << 16);
+        }
+        *reinterpret_cast<u32x4*>(parts + 8 * c) = vh;
+        *reinterpret_cast<u32x4*>(parts + pn + 8 * c) = vm;
+        *reinterpret_cast<u32x4*>(parts + 2 * pn + 8 * c) = vl;
     }
 }
 
-__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ parts,
-                                                          const float* __restrict__ bias,
-                                                          float* __restrict__ logits, int64_t T, int d, int E) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kRBM * kRStride];
-    __shared__ __attribute__((aligned(16))) uint16_t sB[2][3][kRBN * kRStride];
+// out: logits [T, E] (+ bias) when n_split == 1, else partial sums [n_split][T][E].
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void router_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ parts,
+                        const float* __restrict__ bias, float* __restrict__ out, int64_t T, int d, int E,
+                        int n_mblocks, int n_nblocks, int n_split) {
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRtStages * kRtStage];
+    // (token block m, K range r) pairs go to XCD (block id % 8) in turn, each with its expert blocks in a row
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int pair = 8 * (j / n_nblocks) + xcd, nblk = j % n_nblocks;
+    if (pair >= n_mblocks * n_split) return;  // uniform, before any barrier
+    const int mblk = pair / n_split, range = pair % n_split;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave & 3, wn = wave >> 2;
+    const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
+    const int64_t m0 = static_cast<int64_t>(mblk) * kRtBM;
+    const int n0 = nblk * kRtBN;
+    const int eblocks = router_epad(E) / 16;
+    const int64_t pn = static_cast<int64_t>(eblocks) * 16 * d;
+    const uint32_t ring_lds = lds_addr(ring);
+    const int nk_all = d / kRtKS;
+    const int s_lo = static_cast<int>(static_cast<int64_t>(range) * nk_all / n_split);
+    const int s_hi = static_cast<int>(static_cast<int64_t>(range + 1) * nk_all / n_split);
+    const int nk = s_hi - s_lo;  // >= 1: n_split <= nk_all
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n0 = blockIdx.x * kRBN;
-    const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kRBM;
-    const int64_t pn = static_cast<int64_t>(E) * d;  // elements per weight part
-
-    // global -> register staging: 512 16-byte chunks per 64 x 64 tile, two per
-    // thread (rows tid / 8 and tid / 8 + 32, chunk tid % 8); rows past the
-    // matrix end re-read its last row (results never stored)
-    const int ld_row = tid >> 3, ld_col = 8 * (tid & 7);
-    int64_t a_off[2], b_off[2];
+    // this wave's loads per stage: x row blocks 2 wave, 2 wave + 1 (lane: row, K 8 (l / 16));
+    // weight blocks 3 wave .. 3 wave + 2 of the 24 (part p = idx / 8, expert block idx % 8)
+    const uint16_t* a_src[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-        a_off[p] = min(m0 + ld_row + 32 * p, T - 1) * d + ld_col;
-        b_off[p] = static_cast<int64_t>(min(n0 + ld_row + 32 * p, E - 1)) * d + ld_col;
+        const int64_t row = min(m0 + 16 * (2 * wave + p) + frag_row, T - 1);
+        a_src[p] = x + row * d + frag_k + kRtKS * s_lo;
     }
-    u32x4 a_reg[2], b_reg[3][2];
-    auto load_tile = [&](int k0) {
+    const uint16_t* b_src[3];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            a_reg[p] = *reinterpret_cast<const u32x4*>(x + a_off[p] + k0);
+    for (int q = 0; q < 3; ++q) {
+        const int idx = 3 * wave + q;
+        const int eb = min(n0 / 16 + idx % 8, eblocks - 1);  // clamped: such columns are never stored
+        b_src[q] = static_cast<const uint16_t*>(
+            uniform_ptr(parts + (idx / 8) * pn + (static_cast<int64_t>(eb) * (d / 32) + s_lo) * 512));
+    }
+    auto issue = [&](int s) {  // local step s of this K range into ring slot s % kRtStages
+        const uint32_t slot = ring_lds + static_cast<uint32_t>((s % kRtStages) * kRtStage);
 #pragma unroll
-            for (int q = 0; q < 3; ++q) b_reg[q][p] = *reinterpret_cast<const u32x4*>(parts + q * pn + b_off[p] + k0);
-        }
-    };
-    auto store_tile = [&](int buf) {
+        for (int p = 0; p < 2; ++p) dma_vaddr(slot + 1024u * (2 * wave + p), a_src[p] + kRtKS * s);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int off = (ld_row + 32 * p) * kRStride + ld_col;
-            *reinterpret_cast<u32x4*>(&sA[buf][off]) = a_reg[p];
-#pragma unroll
-            for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x4*>(&sB[buf][q][off]) = b_reg[q][p];
-        }
+        for (int q = 0; q < 3; ++q) dma_saddr(slot + kRtAStage + 1024u * (3 * wave + q), b_src[q], 16u * lane + 1024u * s);
     };
 
-    f32x4 acc[2][2];
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
-    const int nk = d / kRBK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int step = 0; step < nk; ++step) {
-        const int cur = step & 1;
-        if (step + 1 < nk) load_tile((step + 1) * kRBK);
+    issue(0);
+    if (nk > 1) issue(1);
+    const uint8_t* a_lds = ring + 1024 * (4 * wm) + 16 * lane;
+    const uint8_t* b_lds = ring + kRtAStage + 1024 * (4 * wn) + 16 * lane;
+    for (int s = 0; s < nk; ++s) {
+        // step s has landed once only step s + 1's loads (if any) are in flight
+        if (s + 1 < nk)
+            wait_barrier<kRtLoads>();
+        else
+            wait_barrier<0>();
+        if (s + 2 < nk) issue(s + 2);
+        const int off = (s % kRtStages) * kRtStage;
+        bf16x8 b[3][4];
 #pragma unroll
-        for (int s = 0; s < kRBK / 32; ++s) {
-            bf16x8 a[2], b[3][2];
+        for (int q = 0; q < 3; ++q)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                a[i] = *reinterpret_cast<const bf16x8*>(&sA[cur][(wm * 32 + i * 16 + frag_row) * kRStride + s * 32 + frag_k]);
+            for (int jn = 0; jn < 4; ++jn)
+                b[q][jn] = *reinterpret_cast<const bf16x8*>(b_lds + off + 1024 * (8 * q + jn));
 #pragma unroll
-            for (int q = 0; q < 3; ++q)
+        for (int i = 0; i < 4; ++i) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(a_lds + off + 1024 * i);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    b[q][j] = *reinterpret_cast<const bf16x8*>(
-                        &sB[cur][q][(wn * 32 + j * 16 + frag_row) * kRStride + s * 32 + frag_k]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    acc[i][j] = mfma_16x16x32(a[i], b[2][j], acc[i][j]);  // smallest part first
-                    acc[i][j] = mfma_16x16x32(a[i], b[1][j], acc[i][j]);
-                    acc[i][j] = mfma_16x16x32(a[i], b[0][j], acc[i][j]);
-                }
+            for (int jn = 0; jn < 4; ++jn) {
+                acc[i][jn] = mfma_16x16x32(a, b[2][jn], acc[i][jn]);  // smallest part first
+                acc[i][jn] = mfma_16x16x32(a, b[1][jn], acc[i][jn]);
+                acc[i][jn] = mfma_16x16x32(a, b[0][jn], acc[i][jn]);
+            }
         }
-        if (step + 1 < nk) store_tile(cur ^ 1);
-        __syncthreads();
     }
 
+    float* dst = n_split == 1 ? out : out + static_cast<int64_t>(range) * T * E;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 32 + j * 16 + (lane & 15);
+    for (int jn = 0; jn < 4; ++jn) {
+        const int col = n0 + 64 * wn + 16 * jn + frag_row;
         if (col >= E) continue;
-        const float bcol = bias ? bias[col] : 0.f;
+        const float bcol = (n_split == 1 && bias) ? bias[col] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t row = m0 + wm * 32 + i * 16 + 4 * (lane >> 4) + q;
-                if (row < T) logits[row * E + col] = acc[i][j][q] + bcol;
+                const int64_t row = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + q;
+                if (row < T) dst[row * E + col] = acc[i][jn][q] + bcol;
             }
+    }
+}
+
+// logits[t, e] = sum over r = 0 .. n_split - 1 of partial[r][t][e] (in that order) + bias[e]; the
+// loads of 8 partials are issued before their adds
+__global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restrict__ partial, int n_split,
+                                                            const float* __restrict__ bias, int64_t n, int E,
+                                                            float* __restrict__ logits) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        float v = partial[i];
+        for (int r0 = 1; r0 < n_split; r0 += 8) {
+            float p[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) p[u] = r0 + u < n_split ? partial[static_cast<int64_t>(r0 + u) * n + i] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (r0 + u < n_split) v += p[u];
+        }
+        logits[i] = v + (bias ? bias[i % E] : 0.f);
     }
 }
 
@@ -189,15 +262,47 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 
 // ------------------------------------------------------------------ launchers
 
-size_t router_parts_bytes(int d, int E) { return sizeof(uint16_t) * 3 * static_cast<size_t>(E) * d; }
+// K ranges: enough (token block, expert block, K range) workgroups to give most
+// CUs one, at most 32 ranges (their partial sums are read back once more), never
+// a range shorter than one K step.
+static int router_split_count(int64_t T, int d, int E) {
+    const int64_t tiles = ((T + kRtBM - 1) / kRtBM) * ((E + kRtBN - 1) / kRtBN);
+    int64_t s = (256 + tiles - 1) / tiles;
+    if (tiles >= 192) s = 1;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(s, 32), d / kRtKS)));
+}
+
+size_t router_ws_bytes(int64_t T, int d, int E) {
+    const size_t parts = sizeof(uint16_t) * 3 * static_cast<size_t>(router_epad(E)) * d;
+    const int S = router_split_count(T, d, E);
+    const size_t partial = S > 1 ? sizeof(float) * static_cast<size_t>(S) * static_cast<size_t>(T) * E : 0;
+    return (parts + 255) / 256 * 256 + partial;
+}
 
 hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bias, float* logits, int64_t T, int d,
-                              int E, uint16_t* parts, hipStream_t stream) {
-    const int64_t n = static_cast<int64_t>(E) * d;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, w, n, parts);
-    dim3 grid((E + kRBN - 1) / kRBN, static_cast<unsigned>((T + kRBM - 1) / kRBM));
-    hipLaunchKernelGGL(router_gemm_kernel, grid, dim3(256), 0, stream, x, parts, bias, logits, T, d, E);
+                              int E, void* ws, hipStream_t stream) {
+    if (T <= 0) return hipSuccess;
+    uint16_t* parts = static_cast<uint16_t*>(ws);
+    float* partial = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                              (sizeof(uint16_t) * 3 * static_cast<size_t>(router_epad(E)) * d + 255) /
+                                                  256 * 256);
+    const int64_t chunks = static_cast<int64_t>(router_epad(E)) * (d / 8);
+    const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 4096);
+    hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, w, E,
+                       router_epad(E), d, parts);
+    const int S = router_split_count(T, d, E);
+    const int n_mblocks = static_cast<int>((T + kRtBM - 1) / kRtBM);
+    const int n_nblocks = (E + kRtBN - 1) / kRtBN;
+    const int64_t pairs = static_cast<int64_t>(n_mblocks) * S;
+    const int64_t grid = static_cast<int64_t>(8) * ((pairs + 7) / 8) * n_nblocks;
+    hipLaunchKernelGGL(router_gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, x, parts, bias,
+                       S == 1 ? logits : partial, T, d, E, n_mblocks, n_nblocks, S);
+    if (S > 1) {
+        const int64_t n = T * E;
+        const int64_t rb = std::min<int64_t>((n + 255) / 256, 8192);
+        hipLaunchKernelGGL(router_reduce_kernel, dim3(static_cast<unsigned>(rb)), dim3(256), 0, stream, partial, S,
+                           bias, n, E, logits);
+    }
     return hipGetLastError();
 }
 
