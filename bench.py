@@ -374,12 +374,25 @@ def latent_bench(args, dev, note):
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    args_c = [ctypes.byref(shape), P(inp.x), P(inp.w_router), None, P(inp.w_proj_down), P(inp.w_gate), P(inp.w_up),
-              P(inp.w_down), P(inp.rms_gain), ctypes.c_float(inp.rms_eps), P(inp.w_proj_up), P(inp.shared_gate),
-              P(inp.shared_up), P(inp.shared_down), P(out), P(ws), ws.numel(), ctypes.c_void_p(stream.cuda_stream)]
+    packed = args.layout == "packed"
+    wts = dict(w_proj_down=inp.w_proj_down, w_gate=inp.w_gate, w_up=inp.w_up, w_down=inp.w_down,
+               w_proj_up=inp.w_proj_up, shared_gate=inp.shared_gate, shared_up=inp.shared_up,
+               shared_down=inp.shared_down)
+    if packed:  # once, before timing; the row-major tensors stay for the check and the CPU baseline
+        from sparse_mixture_experts_fp32_amd import moe_pack_weights
+        for key, w in list(wts.items()):
+            if w is not None:
+                wts[key] = moe_pack_weights(w.unsqueeze(0)).squeeze(0) if w.dim() == 2 else moe_pack_weights(w)
+        torch.cuda.synchronize()
+        note("weights packed into matrix-core tiles")
+    args_c = [ctypes.byref(shape), P(inp.x), P(inp.w_router), None, P(wts["w_proj_down"]), P(wts["w_gate"]),
+              P(wts["w_up"]), P(wts["w_down"]), P(inp.rms_gain), ctypes.c_float(inp.rms_eps), P(wts["w_proj_up"]),
+              P(wts["shared_gate"]), P(wts["shared_up"]), P(wts["shared_down"]), P(out), P(ws), ws.numel(),
+              ctypes.c_void_p(stream.cuda_stream)]
+    fn = lib.lib.moe_latent_forward_packed if packed else lib.lib.moe_latent_forward
 
     def step():
-        lib.check(lib.lib.moe_latent_forward(*args_c))
+        lib.check(fn(*args_c))
 
     for _ in range(args.warmup):
         step()
@@ -397,6 +410,18 @@ def latent_bench(args, dev, note):
     ms = (time.perf_counter() - t0) * 1e3 / K
     gpu_ms = start.elapsed_time(stop) / K
     note(f"{K} timed steps done")
+    if packed:  # the packed step equals moe_latent_forward on the row-major weights, bit for bit
+        ref = torch.empty_like(out)
+        ref_args = list(args_c)
+        for i, key in ((4, "w_proj_down"), (5, "w_gate"), (6, "w_up"), (7, "w_down"), (10, "w_proj_up"),
+                       (11, "shared_gate"), (12, "shared_up"), (13, "shared_down")):
+            ref_args[i] = P(getattr(inp, key))
+        ref_args[14] = P(ref)
+        lib.check(lib.lib.moe_latent_forward(*ref_args))
+        torch.cuda.synchronize()
+        assert torch.equal(ref, out), "packed LatentMoE step and moe_latent_forward disagree"
+        del ref
+        note("packed step equals moe_latent_forward (row-major weights) bit for bit")
     n = T * k
     flops = {"router": 2.0 * T * d * E, "down_projection": 2.0 * T * d * l, "routed_gate_up": 4.0 * n * l * h,
              "routed_down": 2.0 * n * l * h, "up_projection": 2.0 * T * l * d, "shared": 6.0 * S * T * d * hs}
@@ -408,7 +433,8 @@ def latent_bench(args, dev, note):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Stable LatentMoE, T={T} d={d} l={l} E={E} top-{k} h={h}, "
                                f"{S} shared experts of width {hs}, fp32 gate",
-                   "T": T, "d": d, "l": l, "E": E, "k": k, "h": h, "n_shared": S, "h_shared": hs, "seed": cfg.seed},
+                   "T": T, "d": d, "l": l, "E": E, "k": k, "h": h, "n_shared": S, "h_shared": hs, "seed": cfg.seed,
+                   "weight_layout": args.layout},
         "gpu_ms_per_step": gpu_ms,
         "flops": flops,
         "roofline": {"kernel": "whole LatentMoE step (every kernel of moe_latent_forward)", "bound": "mfma",

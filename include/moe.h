@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -380,6 +380,14 @@ int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const
                        const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
                        const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
                        const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream);
+/* moe_latent_forward with every bf16 weight in packed order (moe_pack_weights: w_proj_down as 1 group
+ * [l, d], w_proj_up as 1 group [d, l], the routed and shared expert tensors as E and n_shared groups);
+ * same workspace, bitwise the same out. */
+int moe_latent_forward_packed(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                              const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                              const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                              const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine_rmsnorm -- the routed sum followed by the RMSNorm, in one pass

@@ -81,7 +81,7 @@ __device__ __forceinline__ void ring_mfma(f32x4 (&acc)[kRNB][kMB], const uint8_t
 }
 
 // One (m-tile, n-tile) work item with kMB blocks of 16 rows (M <= 16 kMB).
-template <bool kGated, bool kPacked, int kMB>
+template <bool kGated, bool kPacked, bool kBf16, int kMB>
 __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restrict__ A,
                                           const int32_t* __restrict__ A_rows, int64_t A_nrows, int64_t row0, int M,
                                           const uint16_t* const (&wblk)[kRNB], bool wave_on, int N, int K,
@@ -165,6 +165,10 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
                     const float g = acc[c][i][q], u = acc[kRNB / 2 + c][i][q];
                     crow[16 * c] = f32_to_bf16_bits(g / (1.0f + __expf(-g)) * u);
                 }
+            } else if (kBf16) {  // plain product rounded to bf16 (an operand of a later pass)
+                uint16_t* crow = static_cast<uint16_t*>(Cout) + (row0 + r) * N + n_out + frag_row;
+#pragma unroll
+                for (int j = 0; j < kRNB; ++j) crow[16 * j] = f32_to_bf16_bits(acc[j][i][q]);
             } else {  // Y row: float32
                 float* crow = static_cast<float*>(Cout) + (row0 + r) * N + n_out + frag_row;
 #pragma unroll
@@ -176,7 +180,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
 
 // One workgroup per CU (132 KiB of LDS), so the register allocator may give each
 // of the two waves per SIMD half the register file.
-template <bool kGated, bool kPacked>
+template <bool kGated, bool kPacked, bool kBf16>
 __global__ __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ A_rows, int64_t A_nrows,
                      const int4* __restrict__ tiles, const int32_t* __restrict__ tile_start, int E, int n_tiles,
@@ -224,7 +228,7 @@ void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__
     const int mb = min(kRMaxMB, (M + 15) / 16);
 #define MOE_RING_TILE(NB)                                                                                  \
     if (mb == (NB)) {                                                                                      \
-        ring_tile<kGated, kPacked, (NB)>(ring, A, A_rows, A_nrows, row0, M, wblk, wave_on, N, K, n_out, Cout); \
+        ring_tile<kGated, kPacked, kBf16, (NB)>(ring, A, A_rows, A_nrows, row0, M, wblk, wave_on, N, K, n_out, Cout); \
         return;                                                                                            \
     }
     MOE_RING_TILE(1)
@@ -242,7 +246,7 @@ void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__
 #undef MOE_RING_TILE
 }
 
-template <bool kGated, bool kPacked>
+template <bool kGated, bool kPacked, bool kBf16 = false>
 static hipError_t launch_ring(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows, const int4* tiles,
                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* W0, const uint16_t* W1, int N,
                        int K, void* Cout, hipStream_t stream) {
@@ -251,7 +255,7 @@ static hipError_t launch_ring(const uint16_t* A, const int32_t* A_rows, int64_t 
     const int n_tiles = (N + cols_wg - 1) / cols_wg;
     const int slots = (ffn_max_tiles(n_rows, E) + kXcdsR - 1) / kXcdsR;
     const int64_t grid = static_cast<int64_t>(kXcdsR) * slots * n_tiles;
-    hipLaunchKernelGGL((ffn_ring_kernel<kGated, kPacked>), dim3(static_cast<unsigned>(grid)), dim3(kRThreads), 0,
+    hipLaunchKernelGGL((ffn_ring_kernel<kGated, kPacked, kBf16>), dim3(static_cast<unsigned>(grid)), dim3(kRThreads), 0,
                        stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
     return hipGetLastError();
 }
@@ -275,6 +279,16 @@ hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int3
                                         y_rows, stream);
     return launch_ring<false, false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
                                      y_rows, stream);
+}
+
+hipError_t launch_dense_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                             const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
+                             bool bf16_out, hipStream_t stream) {
+    if (bf16_out)
+        return launch_ring<false, true, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c,
+                                              stream);
+    return launch_ring<false, true, false>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c,
+                                           stream);
 }
 
 // Row-major [rows, K] bf16 -> packed tiles (see the layout above). One thread per

@@ -39,6 +39,10 @@ hipError_t launch_gate_up_ring(const uint16_t* a, const int32_t* a_rows, int64_t
 hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
                             int d, int E, int h, const uint16_t* w_down, float* y_rows, bool packed,
                             hipStream_t stream);
+// plain products c = a w^T per group on packed weights (bf16 or float32 out), as launch_dense
+hipError_t launch_dense_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                             const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
+                             bool bf16_out, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T,
                           int d, int k, int64_t n_rows, float* out, hipStream_t stream);

@@ -643,11 +643,12 @@ int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int
     return hip_status(err, "combine_rmsnorm launch");
 }
 
-int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
-                       const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
-                       const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
-                       const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
-                       const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
+static int latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                          const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                          const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                          const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                          const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream,
+                          bool packed) {
     int st = check_latent_shape(shape);
     if (st != MOE_OK) return st;
     if (!std::isfinite(rms_eps) || rms_eps < 0.f) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
@@ -714,28 +715,48 @@ int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const
             "permute launch");
     // z = x W_down_proj^T (bf16)
     MOE_TRY(moe::launch_build_tiles(dense_off, T, 1, dw.tiles, dw.tile_start, s), "build_tiles launch");
-    MOE_TRY(moe::launch_dense(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s),
+    MOE_TRY(packed ? moe::launch_dense_ring(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s)
+                   : moe::launch_dense(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s),
             "down projection launch");
     // routed experts on z (rows gathered through row_src), then u and RMSNorm(u)
     MOE_TRY(moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s), "build_tiles launch");
-    MOE_TRY(moe::launch_gate_up(z, row_src, T, fw.tiles, fw.tile_start, n, l, E, h, w_gate, w_up, h_act, s),
+    MOE_TRY(moe::launch_gate_up(z, row_src, T, fw.tiles, fw.tile_start, n, l, E, h, w_gate, w_up, h_act, s, packed),
             "gate_up launch");
-    MOE_TRY(moe::launch_down(h_act, fw.tiles, fw.tile_start, n, l, E, h, w_down, y_rows, s), "down launch");
+    MOE_TRY(moe::launch_down(h_act, fw.tiles, fw.tile_start, n, l, E, h, w_down, y_rows, s, packed), "down launch");
     MOE_TRY(moe::launch_combine_rmsnorm(y_rows, row_of, w, T, l, k, n, rms_gain, rms_eps, nullptr, r, s),
             "combine_rmsnorm launch");
     // out = RMSNorm(u) W_up_proj^T (float32) ...
-    MOE_TRY(moe::launch_dense(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s),
+    MOE_TRY(packed ? moe::launch_dense_ring(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s)
+                   : moe::launch_dense(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s),
             "up projection launch");
     if (S > 0) {  // ... + the shared experts on x
         MOE_TRY(moe::launch_build_tiles(shared_off, T * S, S, sw.tiles, sw.tile_start, s), "build_tiles launch");
         MOE_TRY(moe::launch_gate_up(x, shared_rows, T, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_gate,
-                                    shared_up, sh_h, s), "shared gate_up launch");
-        MOE_TRY(moe::launch_down(sh_h, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_down, sh_y, s),
+                                    shared_up, sh_h, s, packed), "shared gate_up launch");
+        MOE_TRY(moe::launch_down(sh_h, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_down, sh_y, s, packed),
                 "shared down launch");
         MOE_TRY(moe::launch_add_shared(out, sh_y, T, d, S, s), "add_shared launch");
     }
 #undef MOE_TRY
     return ok();
+}
+
+int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                       const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                       const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                       const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                       const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
+    return latent_forward(shape, x, w_router, router_bias, w_proj_down, w_gate, w_up, w_down, rms_gain, rms_eps,
+                          w_proj_up, shared_gate, shared_up, shared_down, out, ws, ws_bytes, stream, false);
+}
+
+int moe_latent_forward_packed(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                              const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                              const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                              const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                              const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
+    return latent_forward(shape, x, w_router, router_bias, w_proj_down, w_gate, w_up, w_down, rms_gain, rms_eps,
+                          w_proj_up, shared_gate, shared_up, shared_down, out, ws, ws_bytes, stream, true);
 }
 
 int moe_mx_quantize_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint8_t* q, uint8_t* scales,

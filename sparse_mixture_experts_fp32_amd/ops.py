@@ -323,9 +323,12 @@ def moe_combine_rmsnorm(y_rows, row_of, topk_w, gain, eps: float, want_u: bool =
 
 
 class LatentMoEForward:
-    """moe_latent_forward with a reusable workspace (allocated once per shape)."""
+    """moe_latent_forward (moe_latent_forward_packed when packed: every bf16 weight passed through
+    moe_pack_weights) with a reusable workspace (allocated once per shape)."""
 
-    def __init__(self, T: int, d: int, l: int, E: int, k: int, h: int, n_shared: int, h_shared: int, device):
+    def __init__(self, T: int, d: int, l: int, E: int, k: int, h: int, n_shared: int, h_shared: int, device,
+                 packed: bool = False):
+        self.packed = packed
         self.shape = _lib.latent_shape(T, d, l, E, k, h, n_shared, h_shared)
         self.T, self.d, self.l, self.E, self.k, self.h = T, d, l, E, k, h
         self.S, self.hs = n_shared, h_shared
@@ -353,8 +356,9 @@ class LatentMoEForward:
         if out is None:
             out = torch.empty((T, d), dtype=torch.float32, device=dev)
         _need(out, "out", "f32", (T, d), dev)
+        fn = _lib.lib.moe_latent_forward_packed if self.packed else _lib.lib.moe_latent_forward
         with torch.cuda.device(dev):
-            _lib.check(_lib.lib.moe_latent_forward(
+            _lib.check(fn(
                 ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_proj_down),
                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(rms_gain), rms_eps, _ptr(w_proj_up),
                 _ptr(shared_gate if S > 0 else None), _ptr(shared_up if S > 0 else None),

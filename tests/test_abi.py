@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
               "moe_latent_workspace_bytes", "moe_latent_ws_offset", "moe_combine_rmsnorm",
               "moe_mx_quantize_weights", "moe_mx_quantize_rows", "moe_mx_expert_ffn", "moe_mx_forward",
               "moe_mx_forward_ws_offset", "moe_mx_expert_gate_up", "moe_mx_expert_down",
-              "moe_pack_weights", "moe_expert_gate_up_packed", "moe_expert_down_packed", "moe_forward_packed"]:
+              "moe_pack_weights", "moe_expert_gate_up_packed", "moe_expert_down_packed", "moe_forward_packed",
+              "moe_latent_forward_packed"]:
         assert n in names
 
 
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 7
+    assert L.moe_abi_version() == lib.ABI_VERSION == 8
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"

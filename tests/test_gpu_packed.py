@@ -80,3 +80,56 @@ def test_forward_packed_equals_rowmajor_prefill(dev, moe):
     out = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev, packed=True)(inp.x, inp.w_router, None, *packed)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def _pack_latent(moe, inp):
+    """The LatentMoE layer's bf16 weights in packed order (2-D projections as one group each)."""
+    one = lambda w: moe.moe_pack_weights(w.unsqueeze(0)).squeeze(0)  # noqa: E731
+    S = inp.cfg.n_shared
+    return dict(w_proj_down=one(inp.w_proj_down), w_gate=moe.moe_pack_weights(inp.w_gate),
+                w_up=moe.moe_pack_weights(inp.w_up), w_down=moe.moe_pack_weights(inp.w_down),
+                w_proj_up=one(inp.w_proj_up),
+                shared_gate=moe.moe_pack_weights(inp.shared_gate) if S > 0 else None,
+                shared_up=moe.moe_pack_weights(inp.shared_up) if S > 0 else None,
+                shared_down=moe.moe_pack_weights(inp.shared_down) if S > 0 else None)
+
+
+def _latent_pair(moe, dev, inp):
+    c = inp.cfg
+    ref = moe.LatentMoEForward(c.T, c.d, c.l, c.E, c.k, c.h, c.n_shared, c.h_shared, dev)(inp.x, *inp.args())
+    torch.cuda.synchronize()
+    ref = ref.clone()
+    p = _pack_latent(moe, inp)
+    fwd = moe.LatentMoEForward(c.T, c.d, c.l, c.E, c.k, c.h, c.n_shared, c.h_shared, dev, packed=True)
+    out = fwd(inp.x, inp.w_router, inp.router_bias, p["w_proj_down"], p["w_gate"], p["w_up"], p["w_down"],
+              inp.rms_gain, inp.rms_eps, p["w_proj_up"], p["shared_gate"], p["shared_up"], p["shared_down"])
+    torch.cuda.synchronize()
+    return ref, out
+
+
+LATENT_CASES = {
+    "tiny": dict(),
+    "ragged": dict(T=77, d=384, l=256, E=12, k=3, h=384, n_shared=1, h_shared=128),
+    "no_shared": dict(T=40, n_shared=0),
+    "many_tiles": dict(T=1000, d=512, l=384, E=70, k=4, h=128, n_shared=2, h_shared=256),
+}
+
+
+@pytest.mark.parametrize("case", sorted(LATENT_CASES))
+def test_latent_packed_equals_rowmajor(dev, moe, case):
+    from synthetic import make_latent_inputs, scaled_latent
+    cfg = scaled_latent("latent_tiny", name=f"latent_packed_{case}", **LATENT_CASES[case])
+    print(f"latent packed case {case}: {cfg}", flush=True)
+    inp = make_latent_inputs(cfg, device=dev, gen_device="cpu")
+    ref, out = _latent_pair(moe, dev, inp)
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.slow
+def test_latent_packed_equals_rowmajor_full_size(dev, moe):
+    from synthetic import LATENT_CONFIGS, make_latent_inputs
+    cfg = LATENT_CONFIGS["latent"]
+    print("latent packed full size: drawing inputs", flush=True)
+    inp = make_latent_inputs(cfg, device=dev)
+    ref, out = _latent_pair(moe, dev, inp)
+    assert torch.equal(out, ref)
