@@ -121,7 +121,10 @@ int moe_forward_ws_offset(const moe_shape_t* shape, int slot, size_t* offset);
  *  topk_w      [T, k]  float32 out: softmax probabilities of the selected experts,
  *                      renormalised to sum to 1 (exp(l_j - l_0) / sum_i exp(l_i - l_0))
  *  ws, ws_bytes        workspace of at least moe_workspace_bytes(shape, MOE_CALL_ROUTE)
- *                      (w_router split exactly into three bf16 parts for the matrix cores)
+ *                      (w_router split exactly into three bf16 parts for the matrix cores;
+ *                      for batches too small to fill the GPU, float32 partial sums over
+ *                      up to 32 K ranges, added in range order, so the logits do not
+ *                      depend on scheduling)
  * NaN logits are outside the contract; the ids written are still k distinct
  * experts in [0, E).
  */
