@@ -84,37 +84,51 @@ __global__ __launch_bounds__(kRankWaves * 64) void expert_count_kernel(const int
     }
 }
 
-// One 1024-thread workgroup; thread e owns expert e's nchunks (<= kMaxChunks) counts.
-// Rewrites count[e, c] as the first row of (e, c); expert_offsets[e] = first row of e.
+// One 1024-thread workgroup. Rewrites count[e, c] as the first row of (e, c);
+// expert_offsets[e] = first row of e, expert_offsets[E] = all rows. The E x nchunks
+// counts (<= 1024 x 32) are read and written coalesced through LDS (rows padded to
+// nchunks + 1 words, so thread e's walk along its row is free of bank conflicts);
+// the scan over experts is a wavefront scan (shuffles) plus a scan of the 16
+// wavefront totals.
 __global__ __launch_bounds__(1024) void expert_scan_kernel(int32_t* __restrict__ count, int E, int nchunks,
                                                            int32_t* __restrict__ expert_offsets) {
-    __shared__ int32_t part[1024];
-    const int tid = threadIdx.x;
-    int32_t cnt[kMaxChunks];
-    int32_t total = 0;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-        cnt[c] = (tid < E && c < nchunks) ? count[static_cast<int64_t>(tid) * nchunks + c] : 0;
-        total += cnt[c];
-    }
-    part[tid] = total;
+    __shared__ int32_t cs[kMaxExperts * (kMaxChunks + 1)];
+    __shared__ int32_t wsum[1024 / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int stride = nchunks + 1;
+    const int n = E * nchunks;
+    for (int i = tid; i < n; i += 1024) cs[(i / nchunks) * stride + i % nchunks] = count[i];
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
-        const int32_t v = tid >= off ? part[tid - off] : 0;
-        __syncthreads();
-        part[tid] += v;
-        __syncthreads();
+    int32_t total = 0;
+    if (tid < E)
+        for (int c = 0; c < nchunks; ++c) total += cs[tid * stride + c];
+    // inclusive scan of the totals within the wavefront
+    int32_t incl = total;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
     }
-    int32_t run = part[tid] - total;
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int32_t before = 0;  // totals of the lower wavefronts
+    for (int v = 0; v < wave; ++v) before += wsum[v];
+    int32_t run = before + incl - total;  // exclusive prefix of expert tid
     if (tid < E) {
         expert_offsets[tid] = run;
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) {
-            if (c < nchunks) count[static_cast<int64_t>(tid) * nchunks + c] = run;
-            run += cnt[c];
+        for (int c = 0; c < nchunks; ++c) {
+            const int32_t cnt = cs[tid * stride + c];
+            cs[tid * stride + c] = run;
+            run += cnt;
         }
     }
-    if (tid == 1023) expert_offsets[E] = part[1023];
+    if (tid == 1023) {
+        int32_t all = 0;
+        for (int v = 0; v < 1024 / 64; ++v) all += wsum[v];
+        expert_offsets[E] = all;
+    }
+    __syncthreads();
+    for (int i = tid; i < n; i += 1024) count[i] = cs[(i / nchunks) * stride + i % nchunks];
 }
 
 // One workgroup per chunk: stable ranks, row_of and row_src.
