@@ -394,13 +394,22 @@ static_assert(GateUpCfg::kBM == DownCfg::kBM && DenseCfg::kBM == DownCfg::kBM, "
 
 int ffn_tile_rows() { return GateUpCfg::kBM; }
 
-int ffn_max_tiles(int64_t n_rows, int E) { return max_tiles_for(n_rows, E, ffn_tile_rows()); }
+// Capacity of a tile list: enough for the shortest m-tiles any pass uses (the MX
+// passes' 128 rows), so one workspace serves every pass.
+constexpr int kMinTileRows = 128;
+int ffn_max_tiles(int64_t n_rows, int E) { return max_tiles_for(n_rows, E, kMinTileRows); }
+
+hipError_t launch_build_tiles_rows(const int32_t* expert_offsets, int64_t n_rows, int E, int bm, int4* tiles,
+                                   int32_t* tile_start, hipStream_t stream) {
+    if (bm < kMinTileRows || bm % 16 != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, stream, expert_offsets, E, n_rows, bm,
+                       ffn_max_tiles(n_rows, E), tiles, tile_start);
+    return hipGetLastError();
+}
 
 hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int E, int4* tiles,
                               int32_t* tile_start, hipStream_t stream) {
-    hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(1024), 0, stream, expert_offsets, E, n_rows,
-                       ffn_tile_rows(), ffn_max_tiles(n_rows, E), tiles, tile_start);
-    return hipGetLastError();
+    return launch_build_tiles_rows(expert_offsets, n_rows, E, ffn_tile_rows(), tiles, tile_start, stream);
 }
 
 hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,

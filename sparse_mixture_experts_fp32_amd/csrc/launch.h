@@ -23,6 +23,9 @@ int ffn_tile_rows();
 int ffn_max_tiles(int64_t n_rows, int E);
 hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int E, int4* tiles,
                               int32_t* tile_start, hipStream_t stream);
+// the same with m-tiles of up to bm rows (bm >= 128, a multiple of 16)
+hipError_t launch_build_tiles_rows(const int32_t* expert_offsets, int64_t n_rows, int E, int bm, int4* tiles,
+                                   int32_t* tile_start, hipStream_t stream);
 // a_rows == nullptr: GEMM row r is a[r] (a = x_perm); else it is a[a_rows[r]] (a = x with a_nrows rows).
 hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
                           const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,

@@ -216,10 +216,6 @@ void forward_layout(const moe_shape_t* s, size_t off[kFwdTotal + 1]) {
 int check_mx_shape(const moe_shape_t* s) {
     int st = check_shape(s);
     if (st != MOE_OK) return st;
-    // the MX passes walk the same m-tile list as the bf16 passes
-    if (moe::mx_tile_rows() != moe::ffn_tile_rows())
-        return fail(MOE_ERR_UNSUPPORTED, "MX and bf16 m-tile heights differ (%d vs %d)", moe::mx_tile_rows(),
-                    moe::ffn_tile_rows());
     if (s->d % 512 != 0 || s->h % 512 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "the MX path needs d and h to be multiples of 512 (d = %d, h = %d)", s->d,
                     s->h);
@@ -816,7 +812,7 @@ int moe_mx_expert_ffn(const moe_shape_t* shape, const uint8_t* a_q, const uint8_
     const int64_t n = shape->T * shape->k;
     const int d = shape->d, E = shape->E, h = shape->h;
     const FfnWs fw = ffn_carve(shape, ws);
-    hipError_t err = moe::launch_build_tiles(expert_offsets, n, E, fw.tiles, fw.tile_start, s);
+    hipError_t err = moe::launch_build_tiles_rows(expert_offsets, n, E, moe::mx_tile_rows(), fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
     err = moe::launch_mx_ffn_pass(true, a_q, a_s, a_rows, a_rows ? shape->T : n, fw.tiles, fw.tile_start, n, E,
                                   wg_q, wg_s, wu_q, wu_s, h, d, h_act, s);
@@ -849,7 +845,7 @@ int moe_mx_expert_gate_up(const moe_shape_t* shape, const uint8_t* a_q, const ui
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = shape->T * shape->k;
     const FfnWs fw = ffn_carve(shape, ws);
-    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
+    hipError_t err = moe::launch_build_tiles_rows(expert_offsets, n, shape->E, moe::mx_tile_rows(), fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
     err = moe::launch_mx_ffn_pass(true, a_q, a_s, a_rows, a_rows ? shape->T : n, fw.tiles, fw.tile_start, n,
                                   shape->E, wg_q, wg_s, wu_q, wu_s, shape->h, shape->d, h_act, s);
@@ -873,7 +869,7 @@ int moe_mx_expert_down(const moe_shape_t* shape, const uint8_t* h_q, const uint8
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t n = shape->T * shape->k;
     const FfnWs fw = ffn_carve(shape, ws);
-    hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
+    hipError_t err = moe::launch_build_tiles_rows(expert_offsets, n, shape->E, moe::mx_tile_rows(), fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
     err = moe::launch_mx_ffn_pass(false, h_q, h_s, nullptr, n, fw.tiles, fw.tile_start, n, shape->E, wd_q, wd_s,
                                   nullptr, nullptr, shape->d, shape->h, y_rows, s);
@@ -941,7 +937,7 @@ int moe_mx_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_r
     if (err != hipSuccess) return hip_status(err, "permute launch");
     err = moe::launch_mx_quantize(x, false, T, d, false, x_q, x_s, s);
     if (err != hipSuccess) return hip_status(err, "mx_quantize launch");
-    err = moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s);
+    err = moe::launch_build_tiles_rows(offsets, n, E, moe::mx_tile_rows(), fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
     err = moe::launch_mx_ffn_pass(true, x_q, x_s, row_src, T, fw.tiles, fw.tile_start, n, E, wg_q, wg_s, wu_q, wu_s,
                                   h, d, h_act, s);

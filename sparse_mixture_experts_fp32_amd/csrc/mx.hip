@@ -25,6 +25,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace moe {
 
@@ -137,12 +138,13 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__
 
 // --------------------------------------------------------- grouped GEMM
 //
-// Work unit and schedule as in the bf16 grouped GEMM (m-tiles of up to 192
-// rows of one expert from the device-built tile list, n-tiles of the weight
-// rows, m-tiles of one expert innermost within each XCD's contiguous share).
-// Workgroup: 8 wavefronts; each owns two 16-row blocks of weight rows (gate and
-// up rows of the same 16 outputs for the gate/up pass, 32 output rows for the
-// down pass) and every row of the m-tile. Per K step of 128: the A rows (128
+// Work unit and schedule as in the bf16 grouped GEMM (m-tiles of one expert
+// from the device-built tile list, here of up to 128 rows, n-tiles of the
+// weight rows, m-tiles of one expert innermost within each XCD's contiguous
+// share). Workgroup: 8 wavefronts; each owns four 16-row blocks of weight rows
+// (gate and up rows of the same 32 outputs for the gate/up pass, 64 output rows
+// for the down pass) and every row of the m-tile, so each 32-byte A fragment
+// read from LDS feeds four matrix instructions. Per K step of 128: the A rows (128
 // bytes each) and their four scale bytes are staged in LDS, double-buffered;
 // each lane loads its 16 bytes of E2M1 weights per block straight into
 // registers (one kilobyte per wavefront, contiguous) three steps ahead, and one
@@ -150,9 +152,9 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__
 
 constexpr int kMxWaves = 8;
 constexpr int kMxThreads = kMxWaves * 64;
-constexpr int kMxNB = 2;
+constexpr int kMxNB = 4;
 constexpr int kMxKS = 128;
-constexpr int kMxMaxMB = 12;
+constexpr int kMxMaxMB = 8;
 constexpr int kMxBM = 16 * kMxMaxMB;
 constexpr int kMxARow = kMxKS + 32;  // LDS bytes per staged row: 32 B of padding keeps the 16-byte
                                      // fragment reads of 16 rows conflict-free (16 B measured 39 %
@@ -169,7 +171,8 @@ template <bool kGated, int kMB>
 __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t* __restrict__ A,
                                         const uint8_t* __restrict__ As, const int32_t* __restrict__ A_rows,
                                         int64_t A_nrows, int64_t row0, int M, const uint8_t* const (&wq)[kMxNB],
-                                        const uint8_t* const (&wsc)[kMxNB], bool wave_on, int N, int K, int n_wave,
+                                        const uint8_t* const (&wsc)[kMxNB], uint32_t lane_q, uint32_t lane_s,
+                                        bool wave_on, int N, int K, int n_wave,
                                         float* __restrict__ C) {
     constexpr int kPasses = (16 * kMB + kMxRowsPerPass - 1) / kMxRowsPerPass;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -219,11 +222,11 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
     uint32_t bs[2][kMxNB];     // weight scale words, two sets of four K steps
     auto load_b = [&](u32x4 (&dst)[kMxNB], int s) {
 #pragma unroll
-        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const u32x4*>(wq[b] + s * 1024);
+        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const u32x4*>(wq[b] + (lane_q + s * 1024u));
     };
     auto load_bs = [&](uint32_t (&dst)[kMxNB], int q4) {
 #pragma unroll
-        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const uint32_t*>(wsc[b] + q4 * 256);
+        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const uint32_t*>(wsc[b] + (lane_s + q4 * 256u));
     };
     // multiply one K step from LDS buffer `buf` with weights w and scale byte sel of words ws
     auto step = [&](int buf, const u32x4 (&w)[kMxNB], const uint32_t (&ws)[kMxNB], auto sel) {
@@ -286,14 +289,16 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
     // Every value first, then the stores back to back: a store reads its data and
     // address registers after issue, so interleaving each store with the next
     // value's arithmetic would make the compiler wait for every store to finish.
-    if (kGated) {  // H row (float32): gate block 0, up block 1
+    if (kGated) {  // H row (float32): gate blocks 0 .. kMxNB / 2 - 1, then the same rows of up
 #pragma unroll
-        for (int i = 0; i < kMB; ++i)
+        for (int c = 0; c < kMxNB / 2; ++c)
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const float g = acc[0][i][qq], u = acc[1][i][qq];
-                acc[0][i][qq] = g / (1.0f + __expf(-g)) * u;
-            }
+            for (int i = 0; i < kMB; ++i)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    const float g = acc[c][i][qq], u = acc[kMxNB / 2 + c][i][qq];
+                    acc[c][i][qq] = g / (1.0f + __expf(-g)) * u;
+                }
     }
     float* cbase = C + row0 * N + n_wave + fr;
 #pragma unroll
@@ -304,7 +309,8 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
             if (r >= M) continue;
             float* crow = cbase + static_cast<int64_t>(r) * N;
             if (kGated) {
-                crow[0] = acc[0][i][qq];
+#pragma unroll
+                for (int c = 0; c < kMxNB / 2; ++c) crow[16 * c] = acc[c][i][qq];
             } else {
 #pragma unroll
                 for (int b = 0; b < kMxNB; ++b) crow[16 * b] = acc[b][i][qq];
@@ -320,7 +326,7 @@ void mx_grouped_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
                        const int32_t* __restrict__ tile_start, int E, int n_tiles, const uint8_t* __restrict__ W0q,
                        const uint8_t* __restrict__ W0s, const uint8_t* __restrict__ W1q,
                        const uint8_t* __restrict__ W1s, int N, int K, float* __restrict__ C) {
-    constexpr int kColsW = kGated ? 16 : 32;
+    constexpr int kColsW = kGated ? 16 * kMxNB / 2 : 16 * kMxNB;
     constexpr int kColsWG = kColsW * kMxWaves;
     __shared__ __attribute__((aligned(16))) uint8_t sA[2 * kMxBM * kMxARow];
     __shared__ uint32_t sS[2 * kMxBM];
@@ -349,29 +355,32 @@ void mx_grouped_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     const int n_safe = wave_on ? n_wave : 0;
     const int fr = lane & 15, fg = lane >> 4;
     const int64_t wrows = static_cast<int64_t>(e) * N;  // first weight row of expert e
+    // each block's tile row (16 weight rows) starts at a wave-uniform address; a lane's operand
+    // sits at a fixed offset inside every 1 KiB tile (and every 256-byte scale group)
     const uint8_t* wq[kMxNB];
     const uint8_t* wsc[kMxNB];
 #pragma unroll
     for (int b = 0; b < kMxNB; ++b) {
-        const uint8_t* q = kGated ? (b == 0 ? W0q : W1q) : W0q;
-        const uint8_t* s = kGated ? (b == 0 ? W0s : W1s) : W0s;
-        const int64_t n = wrows + n_safe + (kGated ? 0 : 16 * b) + fr;
-        wq[b] = q + wcode_offset(n, 0, K) + 16 * fg;   // K step s: + s * 1024
-        wsc[b] = s + wscale_offset(n, 0, K) + 4 * fg;  // four K steps q4: + q4 * 256
+        const bool up = kGated && b >= kMxNB / 2;  // gate/up: blocks 0 .. kMxNB / 2 - 1 gate, then up
+        const uint8_t* q = up ? W1q : W0q;
+        const uint8_t* s = up ? W1s : W0s;
+        const int64_t n0 = wrows + n_safe + 16 * (kGated ? b % (kMxNB / 2) : b);  // a multiple of 16
+        wq[b] = static_cast<const uint8_t*>(uniform_ptr(q + wcode_offset(n0, 0, K)));
+        wsc[b] = static_cast<const uint8_t*>(uniform_ptr(s + wscale_offset(n0, 0, K)));
     }
-
-    const int mb = min(kMxMaxMB, (M + 31) / 32 * 2);
+    const uint32_t lane_q = 64u * fr + 16u * fg;  // K step s: + s * 1024
+    const uint32_t lane_s = 16u * fr + 4u * fg;   // four K steps q4: + q4 * 256
+    const int mb = min(kMxMaxMB, (M + 31) / 32 * 2);  // 2, 4, 6 or 8 blocks
 #define MOE_MX_TILE(NB)                                                                                   \
     if (mb == (NB)) {                                                                                     \
-        mx_tile<kGated, (NB)>(sA, sS, A, As, A_rows, A_nrows, row0, M, wq, wsc, wave_on, N, K, n_wave, C); \
+        mx_tile<kGated, (NB)>(sA, sS, A, As, A_rows, A_nrows, row0, M, wq, wsc, lane_q, lane_s, wave_on, N, K, n_wave, \
+                              C);                                                                         \
         return;                                                                                           \
     }
     MOE_MX_TILE(2)
     MOE_MX_TILE(4)
     MOE_MX_TILE(6)
     MOE_MX_TILE(8)
-    MOE_MX_TILE(10)
-    MOE_MX_TILE(12)
 #undef MOE_MX_TILE
 }
 
@@ -402,7 +411,7 @@ hipError_t launch_mx_ffn_pass(bool gated, const uint8_t* a, const uint8_t* a_sca
                               int64_t a_nrows, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int E,
                               const uint8_t* w0q, const uint8_t* w0s, const uint8_t* w1q, const uint8_t* w1s, int N,
                               int K, float* c, hipStream_t stream) {
-    const int cols_wg = (gated ? 16 : 32) * kMxWaves;
+    const int cols_wg = (gated ? 16 * kMxNB / 2 : 16 * kMxNB) * kMxWaves;
     const int n_tiles = (N + cols_wg - 1) / cols_wg;
     const int slots = (ffn_max_tiles(n_rows, E) + kXcdsMx - 1) / kXcdsMx;
     const int64_t grid = static_cast<int64_t>(kXcdsMx) * slots * n_tiles;
