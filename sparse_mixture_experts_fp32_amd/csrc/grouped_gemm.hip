@@ -35,6 +35,10 @@
 // side by side on one XCD and fetch those weights from HBM once (the others
 // hit in L2), and all n-tiles of an expert follow each other, so its A rows
 // stay in that L2 as well.
+//
+// This kernel serves row-major expert weights and the dense passes of the
+// latent layer; packed weights run on the LDS-ring kernel (ffn_ring.hip). Both
+// walk the m-tile list that build_tiles_kernel below writes.
 #include "device_common.h"
 #include "launch.h"
 
