@@ -662,7 +662,7 @@ def main():
     down_gbs = down_bytes / (down_ms * 1e-3) / 1e9
     ms = wall_ms
     # the gate/up kernel: the LDS-ring kernel on packed weights, the register-streaming one on row-major
-    gu_name = ("ffn_ring_kernel<true, true, false>" if packed else
+    gu_name = ("ffn_ring_kernel<true, false>" if packed else
                "grouped_ffn_kernel<moe::GemmCfg<1, 8, 2, 64, 12, true, 16>, true, false>")
     gu_kernel = gu_name + (" (gate/up pass + SwiGLU, packed weights)" if packed else " (gate/up pass + SwiGLU)")
     result = {

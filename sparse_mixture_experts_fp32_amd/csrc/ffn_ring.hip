@@ -81,7 +81,7 @@ __device__ __forceinline__ void ring_mfma(f32x4 (&acc)[kRNB][kMB], const uint8_t
 }
 
 // One (m-tile, n-tile) work item with kMB blocks of 16 rows (M <= 16 kMB).
-template <bool kGated, bool kPacked, bool kBf16, int kMB>
+template <bool kGated, bool kBf16, int kMB>
 __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restrict__ A,
                                           const int32_t* __restrict__ A_rows, int64_t A_nrows, int64_t row0, int M,
                                           const uint16_t* const (&wblk)[kRNB], bool wave_on, int N, int K,
@@ -102,10 +102,9 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
         const int64_t src = A_rows ? min(max(static_cast<int64_t>(A_rows[r]), int64_t(0)), A_nrows - 1) : r;
         a_src[p] = A + src * K + frag_k;
     }
-    // weight loads: packed, the stage's 1 KiB of block j is contiguous (lane l at 16 l);
-    // row-major, lane l reads row l % 16 of the block at K 8 (l / 16)
-    const uint32_t w_lane = kPacked ? 16u * lane : static_cast<uint32_t>(frag_row) * K * 2u + 2u * frag_k;
-    constexpr uint32_t kWStep = kPacked ? 1024u : 2u * kRKS;  // bytes per K step
+    // weight loads: the stage's 1 KiB of block j is contiguous (lane l at 16 l)
+    const uint32_t w_lane = 16u * lane;
+    constexpr uint32_t kWStep = 1024u;  // bytes per K step
 
     auto issue = [&](int s) {  // loads of K step s into ring slot s % 3
         const uint32_t slot = ring_lds + static_cast<uint32_t>((s % kRStages) * kRStage);
@@ -180,7 +179,7 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
 
 // One workgroup per CU (132 KiB of LDS), so the register allocator may give each
 // of the two waves per SIMD half the register file.
-template <bool kGated, bool kPacked, bool kBf16>
+template <bool kGated, bool kBf16>
 __global__ __launch_bounds__(kRThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ A_rows, int64_t A_nrows,
                      const int4* __restrict__ tiles, const int32_t* __restrict__ tile_start, int E, int n_tiles,
@@ -220,15 +219,15 @@ void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__
     for (int b = 0; b < kRNB; ++b) {
         const int row = wave_on ? (kGated ? n_out + 16 * (b % (kRNB / 2)) : n_out + 16 * b) : 0;
         const uint16_t* base = (kGated && b >= kRNB / 2) ? W1 : W0;
-        // packed: block row / 16 starts at (row / 16) * (K / 32) tiles of 512; row-major: at row * K
-        const int64_t off = kPacked ? static_cast<int64_t>(row / 16) * (K / kRKS) * 512 : static_cast<int64_t>(row) * K;
+        // the tiles of rows row .. row + 15 start at (row / 16) * (K / 32) tiles of 512 elements
+        const int64_t off = static_cast<int64_t>(row / 16) * (K / kRKS) * 512;
         wblk[b] = static_cast<const uint16_t*>(uniform_ptr(base + wexp + off));
     }
 
     const int mb = min(kRMaxMB, (M + 15) / 16);
 #define MOE_RING_TILE(NB)                                                                                  \
     if (mb == (NB)) {                                                                                      \
-        ring_tile<kGated, kPacked, kBf16, (NB)>(ring, A, A_rows, A_nrows, row0, M, wblk, wave_on, N, K, n_out, Cout); \
+        ring_tile<kGated, kBf16, (NB)>(ring, A, A_rows, A_nrows, row0, M, wblk, wave_on, N, K, n_out, Cout);        \
         return;                                                                                            \
     }
     MOE_RING_TILE(1)
@@ -246,7 +245,7 @@ void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__
 #undef MOE_RING_TILE
 }
 
-template <bool kGated, bool kPacked, bool kBf16 = false>
+template <bool kGated, bool kBf16 = false>
 static hipError_t launch_ring(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows, const int4* tiles,
                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* W0, const uint16_t* W1, int N,
                        int K, void* Cout, hipStream_t stream) {
@@ -255,40 +254,29 @@ static hipError_t launch_ring(const uint16_t* A, const int32_t* A_rows, int64_t 
     const int n_tiles = (N + cols_wg - 1) / cols_wg;
     const int slots = (ffn_max_tiles(n_rows, E) + kXcdsR - 1) / kXcdsR;
     const int64_t grid = static_cast<int64_t>(kXcdsR) * slots * n_tiles;
-    hipLaunchKernelGGL((ffn_ring_kernel<kGated, kPacked, kBf16>), dim3(static_cast<unsigned>(grid)), dim3(kRThreads), 0,
+    hipLaunchKernelGGL((ffn_ring_kernel<kGated, kBf16>), dim3(static_cast<unsigned>(grid)), dim3(kRThreads), 0,
                        stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
     return hipGetLastError();
 }
 
 hipError_t launch_gate_up_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
                                const int32_t* tile_start, int64_t n_rows, int d, int E, int h,
-                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, bool packed,
-                               hipStream_t stream) {
-    if (packed)
-        return launch_ring<true, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act,
-                                       stream);
-    return launch_ring<true, false>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act,
-                                    stream);
+                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, hipStream_t stream) {
+    return launch_ring<true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act, stream);
 }
 
 hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
-                            int d, int E, int h, const uint16_t* w_down, float* y_rows, bool packed,
-                            hipStream_t stream) {
-    if (packed)
-        return launch_ring<false, true>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
-                                        y_rows, stream);
-    return launch_ring<false, false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
-                                     y_rows, stream);
+                            int d, int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream) {
+    return launch_ring<false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h, y_rows,
+                              stream);
 }
 
 hipError_t launch_dense_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
                              const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
                              bool bf16_out, hipStream_t stream) {
     if (bf16_out)
-        return launch_ring<false, true, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c,
-                                              stream);
-    return launch_ring<false, true, false>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c,
-                                           stream);
+        return launch_ring<false, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c, stream);
+    return launch_ring<false, false>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c, stream);
 }
 
 // Row-major [rows, K] bf16 -> packed tiles (see the layout above). One thread per

@@ -420,15 +420,14 @@ hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nr
                           const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,
                           const uint16_t* w_up, uint16_t* h_act, hipStream_t stream, bool packed) {
     if (packed)
-        return launch_gate_up_ring(a, a_rows, a_nrows, tiles, tile_start, n_rows, d, E, h, w_gate, w_up, h_act, true,
-                                   stream);
+        return launch_gate_up_ring(a, a_rows, a_nrows, tiles, tile_start, n_rows, d, E, h, w_gate, w_up, h_act, stream);
     return launch_ffn<GateUpCfg, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act,
                                        stream);
 }
 
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream, bool packed) {
-    if (packed) return launch_down_ring(h_act, tiles, tile_start, n_rows, d, E, h, w_down, y_rows, true, stream);
+    if (packed) return launch_down_ring(h_act, tiles, tile_start, n_rows, d, E, h, w_down, y_rows, stream);
     return launch_ffn<DownCfg, false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h,
                                       y_rows, stream);
 }

@@ -34,14 +34,12 @@ hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* 
                        int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream, bool packed = false);
 // row-major bf16 [rows, K] (rows % 16 == 0, K % 32 == 0) -> packed 16 x 32 fragment-order tiles
 hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int K, uint16_t* out, hipStream_t stream);
-// the expert passes on the LDS-ring kernel (packed or row-major weights; same tile list and results)
+// the expert passes on the LDS-ring kernel (packed weights; the same tile list as launch_gate_up/launch_down)
 hipError_t launch_gate_up_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
                                const int32_t* tile_start, int64_t n_rows, int d, int E, int h,
-                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, bool packed,
-                               hipStream_t stream);
+                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, hipStream_t stream);
 hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
-                            int d, int E, int h, const uint16_t* w_down, float* y_rows, bool packed,
-                            hipStream_t stream);
+                            int d, int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream);
 // plain products c = a w^T per group on packed weights (bf16 or float32 out), as launch_dense
 hipError_t launch_dense_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
                              const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
