@@ -54,7 +54,7 @@ def parse():
                     help="expert weight format: bf16, or MXFP4 weights with MXFP8 activations (weights quantised "
                          "once before the timed steps)")
     ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed",
-                    help="bf16 expert weight layout: packed into 16 x 64 matrix-core tiles once before the timed "
+                    help="bf16 expert weight layout: packed into 16 x 32 matrix-core tiles once before the timed "
                          "steps (moe_pack_weights), or row-major [E, N, K]; both give the same output bit for bit")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the steps, run a plain float32 copy kernel (out = -in) over this many MiB three "
@@ -366,7 +366,11 @@ def latent_bench(args, dev, note):
 
     cfg = LATENT_CONFIGS[args.workload]
     T, d, l, E, k, h, S, hs = cfg.T, cfg.d, cfg.l, cfg.E, cfg.k, cfg.h, cfg.n_shared, cfg.h_shared
-    inp = make_latent_inputs(cfg, device=dev, progress=lambda n: note(f"drew {n} of {E} experts' weights"))
+    def progress(n):
+        torch.cuda.synchronize()  # the line reports finished draws
+        note(f"drew {n} of {E} experts' weights")
+
+    inp = make_latent_inputs(cfg, device=dev, progress=progress)
     torch.cuda.synchronize()
     note("inputs ready")
     shape = lib.latent_shape(T, d, l, E, k, h, S, hs)
@@ -586,11 +590,15 @@ def main():
         return
     cfg = CONFIGS[args.workload]
     def progress(n):
+        # wait for the draws so that the line reports finished work (under a
+        # counter-collecting profiler every one of the draw's thousands of small
+        # kernels is serialised, and the draw can take minutes)
+        torch.cuda.synchronize()
         print(f"[bench] {cfg.name}: drew {n} of {cfg.E} experts' weights", file=sys.stderr, flush=True)
 
     inp = make_inputs(cfg, device=dev, progress=progress)
-    print(f"[bench] {cfg.name}: inputs ready", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: inputs ready", file=sys.stderr, flush=True)
     note = lambda msg: print(f"[bench] {cfg.name}: {msg}", file=sys.stderr, flush=True)  # noqa: E731
     if args.experts == "mxfp4":
         result = mx_bench(args, lib, inp, cfg, dev, note)

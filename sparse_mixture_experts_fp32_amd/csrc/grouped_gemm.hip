@@ -99,8 +99,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int32_t* __rest
     if (tid < E) tile_start[tid] = min(start, max_tiles);
     if (tid == 1023) tile_start[E] = min(part[1023], max_tiles);
     if (nt > 0) {
-        // nearly equal tiles, each a multiple of 16 rows except the last
-        const int per = ((cnt + nt - 1) / nt + 15) / 16 * 16;
+        // equal tiles (within one row): the workgroups that stream the same
+        // expert's weights for different m-tiles then do the same work, stay in
+        // step and share those weights through L2 (tiles rounded to 16 rows
+        // drifted apart and re-read them from HBM)
+        const int per = (cnt + nt - 1) / nt;
         for (int i = 0; i < nt; ++i) {
             const int r0 = i * per;
             const int rows = max(0, min(per, cnt - r0));
@@ -379,7 +382,8 @@ hipError_t launch_ffn(const uint16_t* A, const int32_t* A_rows, int64_t A_nrows,
                   "the block-count dispatch covers up to 8 steps");
     const int cols_wg = (kGated ? C::kWRows / 2 : C::kWRows) * C::kWN;
     const int n_tiles = (N + cols_wg - 1) / cols_wg;
-    const int slots = (max_tiles_for(n_rows, E, C::kBM) + kXcds - 1) / kXcds;
+    // sized for any tile list (tiles of at least kMinTileRows rows); surplus workgroups exit
+    const int slots = (ffn_max_tiles(n_rows, E) + kXcds - 1) / kXcds;
     const int64_t grid = static_cast<int64_t>(kXcds) * slots * n_tiles;
     hipLaunchKernelGGL((grouped_ffn_kernel<C, kGated, kBf16>), dim3(static_cast<unsigned>(grid)), dim3(C::kThreads), 0, stream, A, A_rows, A_nrows, tiles, tile_start, E, n_tiles, W0, W1, N, K, Cout);
     return hipGetLastError();

@@ -165,9 +165,10 @@ def moe_combine(y_rows, row_of, topk_w):
 
 
 def moe_pack_weights(w):
-    """Expert weights w [G, N, K] bf16 in matrix-core order (16-row x 64-column tiles of
-    1024 contiguous elements): the same values, a new tensor of the same shape whose
-    memory is in packed order (for MoEForward(..., packed=True) and the *_packed calls)."""
+    """Expert weights w [G, N, K] bf16 in matrix-core order (16-row x 32-column tiles of
+    512 contiguous elements, each one MFMA operand in lane order): the same values, a new
+    tensor of the same shape whose memory is in packed order (for
+    MoEForward(..., packed=True) and the *_packed calls)."""
     _need(w, "w", "bf16")
     dev = w.device
     G, N, K = w.shape
