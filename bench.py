@@ -115,6 +115,39 @@ class Layer:
         c(L.moe_combine(sh, P(self.y_rows), P(self.row_of), P(self.w), P(self.out), sp))
 
 
+def time_hbm_kernels(layer, reps):
+    """Mean time of the routing top-k, permute and combine calls, each on its own, on the step's
+    buffers (HIP events on the layer's stream; each rewrites the values the step wrote), and the
+    rate of each in algorithmic bytes: every input read once, every output written once."""
+    import torch
+    L, P, sh, sp, c = layer.lib.lib, layer.P, layer.sh, layer.sp, layer.lib.check
+    cfg = layer.cfg
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    calls = {
+        "topk_softmax": (lambda: c(L.moe_topk_softmax(sh, P(layer.logits), P(layer.idx), P(layer.w), sp)),
+                         4.0 * T * E + 8.0 * T * k, "hbm"),
+        "permute": (lambda: c(L.moe_permute(sh, None, P(layer.idx), P(layer.offsets), P(layer.row_of),
+                                            P(layer.row_src), None, P(layer.ws_perm), layer.ws_perm.numel(), sp)),
+                    4.0 * T * k + 4.0 * (E + 1) + 8.0 * T * k, "latency"),
+        "combine": (lambda: c(L.moe_combine(sh, P(layer.y_rows), P(layer.row_of), P(layer.w), P(layer.out), sp)),
+                    4.0 * T * k * d + 8.0 * T * k + 4.0 * T * d, "hbm"),
+    }
+    out = {"reps": reps}
+    for name, (call, nbytes, bound) in calls.items():
+        for _ in range(3):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(layer.stream)
+            call()
+            b.record(layer.stream)
+        torch.cuda.synchronize()
+        us = sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "bytes": nbytes, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "bound": bound}
+    return out
+
+
 class Balance:
     """Buffers and C-ABI calls of the load-balancing step on a layer's logits."""
 
@@ -698,6 +731,12 @@ def main():
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
                      "traffic": measured_traffic(cfg.name, gu_name), "algorithmic_bytes": gu_bytes},
     }
+    out_before = layer.out.clone()
+    result["hbm_kernels"] = time_hbm_kernels(layer, max(K, 10))
+    torch.cuda.synchronize()
+    assert torch.equal(out_before, layer.out), "re-running route / permute / combine changed the output"
+    del out_before
+    note("top-k, permute and combine timed on their own")
     result["balance"] = Balance(layer).measure(max(K, 10))
     note("load-balancing calls timed")
     if args.cpu_experts > 0:

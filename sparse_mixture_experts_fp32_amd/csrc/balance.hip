@@ -43,11 +43,14 @@ __global__ __launch_bounds__(256) void qb_select_kernel(const float* __restrict_
     if (t >= T) return;  // whole wavefront
     const float* row = logits + t * E;
 
+    float v[NPER], b[NPER];
+    load_row_strided<NPER>(row, E, 0.f, v);
+    load_row_strided<NPER>(bias, E, 0.f, b);
     uint64_t key[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + 64 * i;
-        key[i] = (e < E) ? ((static_cast<uint64_t>(order_key(row[e] + bias[e])) << 32) |
+        key[i] = (e < E) ? ((static_cast<uint64_t>(order_key(v[i] + b[i])) << 32) |
                             (0xffffffffu - static_cast<uint32_t>(e)))
                          : 0ull;
     }
@@ -209,13 +212,10 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
         if (t >= T) break;  // whole wavefront
         const float* row = logits + t * E;
         float v[NPER];
+        load_row_strided<NPER>(row, E, -INFINITY, v);
         float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-            const int e = lane + 64 * i;
-            v[i] = e < E ? row[e] : -INFINITY;
-            mx = fmaxf(mx, v[i]);
-        }
+        for (int i = 0; i < NPER; ++i) mx = fmaxf(mx, v[i]);
         mx = wave_max_f32(mx);
         float s = 0.f;
 #pragma unroll

@@ -240,11 +240,13 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
     if (t >= T) return;
     const float* row = logits + t * E;
 
+    float v[NPER];
+    load_row_strided<NPER>(row, E, 0.f, v);
     uint64_t key[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
         const int e = lane + 64 * i;
-        key[i] = (e < E) ? ((static_cast<uint64_t>(order_key(row[e])) << 32) | (0xffffffffu - static_cast<uint32_t>(e)))
+        key[i] = (e < E) ? ((static_cast<uint64_t>(order_key(v[i])) << 32) | (0xffffffffu - static_cast<uint32_t>(e)))
                          : 0ull;
     }
     // lane j < k: the j-th largest key

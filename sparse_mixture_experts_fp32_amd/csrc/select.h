@@ -22,6 +22,20 @@
 
 namespace moe {
 
+// v[i] = row[lane + 64 i] for i < NPER, or `fill` past the row's end (n entries).
+// Every load reads a clamped index inside the row, so none sits behind a branch and
+// all NPER are in flight together; a load under `if (e < n)` would be followed by its
+// own wait, one memory round trip per element.
+template <int NPER>
+__device__ __forceinline__ void load_row_strided(const float* __restrict__ row, int n, float fill, float (&v)[NPER]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) v[i] = row[min(lane + 64 * i, n - 1)];
+#pragma unroll
+    for (int i = 0; i < NPER; ++i)
+        if (lane + 64 * i >= n) v[i] = fill;
+}
+
 constexpr int kSelectLds = 128;  // uint64 entries of LDS per wavefront (two arrays of 64)
 
 template <int NPER>
