@@ -1,17 +1,19 @@
-// Wavefront top-K of up to 64 * NPER 64-bit keys (one wavefront per token).
+// Wavefront top-K of up to 64 * NPER keys (one wavefront per token).
 //
-// Each lane holds NPER keys (0 = absent); a key's upper 32 bits order the value,
-// its lower 32 bits are ~id, so keys are distinct and the largest key is the
-// largest value with ties to the lower id. select_top leaves, in lane j < K, the
-// j-th largest key.
+// Element i of lane l is expert e = l + 64 i (valid when e < E). Its 64-bit key
+// is (value key << 32) | ~e, with the value key from order_key, so keys are
+// distinct and the largest key is the largest value with ties to the lower id.
+// select_top leaves, in lane j < K, the j-th largest key.
 //
 // Instead of K rounds of "local maximum over NPER keys, wavefront maximum,
 // clear the winner" (K * NPER work per lane), a threshold prunes first:
-//   1. tau = the K-th largest of the 64 lanes' largest value halves, found bit
-//      by bit with ballots. At least K keys have a value half >= tau (those
-//      lane maxima), so every one of the K largest keys has value half >= tau.
-//   2. The keys with value half >= tau (the candidates) are compacted into a
-//      64-entry LDS array of the wavefront with ballot prefix counts.
+//   1. tau = the K-th largest of the 64 lanes' largest value keys, found bit
+//      by bit with ballots. At least K keys have a value key >= tau (those
+//      lane maxima), so every one of the K largest keys has value key >= tau.
+//   2. The keys with value key >= tau (the candidates) are compacted into a
+//      64-entry LDS array of the wavefront: the ballot of each element index is
+//      the write mask, and each writing lane's slot is the count of writing
+//      lanes below it (mbcnt).
 //   3. Each candidate counts the candidates above it (its rank) by reading the
 //      array back (one broadcast read per candidate); the candidate of rank j
 //      is written to entry j of a second array and lane j reads it.
@@ -22,51 +24,58 @@
 
 namespace moe {
 
-// v[i] = row[lane + 64 i] for i < NPER, or `fill` past the row's end (n entries).
-// Every load reads a clamped index inside the row, so none sits behind a branch and
-// all NPER are in flight together; a load under `if (e < n)` would be followed by its
-// own wait, one memory round trip per element.
+// v[i] = row[lane + 64 i] for i < NPER, or `fill` past the row's end (n entries,
+// n > 64 (NPER - 1), so only the last element can be past it). The first NPER - 1
+// loads share one address with immediate offsets and the last reads a clamped
+// index, so none sits behind a branch and all NPER are in flight together; a load
+// under `if (e < n)` would be followed by its own wait, one memory round trip per
+// element.
 template <int NPER>
 __device__ __forceinline__ void load_row_strided(const float* __restrict__ row, int n, float fill, float (&v)[NPER]) {
     const int lane = threadIdx.x & 63;
+    const float* p = row + lane;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) v[i] = row[min(lane + 64 * i, n - 1)];
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-        if (lane + 64 * i >= n) v[i] = fill;
+    for (int i = 0; i < NPER - 1; ++i) v[i] = p[64 * i];
+    const int last = lane + 64 * (NPER - 1);
+    v[NPER - 1] = row[min(last, n - 1)];
+    if (last >= n) v[NPER - 1] = fill;
 }
 
 constexpr int kSelectLds = 128;  // uint64 entries of LDS per wavefront (two arrays of 64)
 
+// vk[i]: value key of element i (order_key of its score); E: valid elements
+// (64 (NPER - 1) < E <= 64 NPER); K <= E.
 template <int NPER>
-__device__ __forceinline__ uint64_t select_top(uint64_t (&key)[NPER], int K, uint64_t* lds) {
+__device__ __forceinline__ uint64_t select_top(const uint32_t (&vk)[NPER], int E, int K, uint64_t* lds) {
     const int lane = threadIdx.x & 63;
-    const uint64_t below = (1ull << lane) - 1ull;
-    // 1. tau over the lanes' largest value halves
-    uint32_t m = 0u;
+    const bool last_on = lane + 64 * (NPER - 1) < E;  // only the last element can be padding
+    auto key_of = [&](int i) {
+        return (static_cast<uint64_t>(vk[i]) << 32) | (0xffffffffu - static_cast<uint32_t>(lane + 64 * i));
+    };
+    // 1. tau over the lanes' largest value keys (padding counts as 0)
+    uint32_t m = last_on ? vk[NPER - 1] : 0u;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) m = max(m, static_cast<uint32_t>(key[i] >> 32));
+    for (int i = 0; i < NPER - 1; ++i) m = max(m, vk[i]);
     uint32_t tau = 0u;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = tau | (1u << b);
         if (__popcll(__ballot(m >= cand)) >= K) tau = cand;
     }
-    // 2. candidates and their count
+    // 2. candidates, compacted in (element, lane) order while they are counted
     int total = 0;
-    uint64_t ball[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
-        ball[i] = __ballot(key[i] != 0ull && static_cast<uint32_t>(key[i] >> 32) >= tau);
-        total += __popcll(ball[i]);
+        const bool c = vk[i] >= tau && (i < NPER - 1 || last_on);
+        const uint64_t bal = __ballot(c);
+        if (c && total + __popcll(bal) <= 64) {
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+            lds[total + static_cast<int>(below)] = key_of(i);
+        }
+        total += __popcll(bal);
     }
     uint64_t mine = 0ull;
     if (total <= 64) {
-        int base = 0;
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-            if ((ball[i] >> lane) & 1ull) lds[base + __popcll(ball[i] & below)] = key[i];
-            base += __popcll(ball[i]);
-        }
         __builtin_amdgcn_wave_barrier();
         // 3. ranks, then the candidates in rank order
         const uint64_t my = lane < total ? lds[lane] : 0ull;
@@ -77,6 +86,9 @@ __device__ __forceinline__ uint64_t select_top(uint64_t (&key)[NPER], int K, uin
         __builtin_amdgcn_wave_barrier();
         mine = lane < K ? lds[64 + lane] : 0ull;
     } else {
+        uint64_t key[NPER];
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) key[i] = (i < NPER - 1 || last_on) ? key_of(i) : 0ull;
         for (int j = 0; j < K; ++j) {
             uint64_t best = key[0];
 #pragma unroll
