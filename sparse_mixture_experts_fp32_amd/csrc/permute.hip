@@ -26,7 +26,7 @@ namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxChunks = 32;
-constexpr int kRankWaves = 8;
+constexpr int kRankWaves = 16;
 
 // Mask of the lanes whose key equals this lane's key (keys below 2^nbits).
 __device__ __forceinline__ uint64_t same_key_lanes(uint32_t key, int nbits, uint64_t active) {
@@ -48,19 +48,37 @@ __device__ __forceinline__ void wave_slice(int64_t n_assign, int chunk, int c, i
     hi = min(lo + per, c1);
 }
 
+// ids of assignments a0 + 64 u + lane (u < kIdBatch), -1 at and past hi (a0 < hi).
+// All kIdBatch loads read a clamped index and are in flight together: one
+// memory round trip per batch instead of one per 64 assignments.
+constexpr int kIdBatch = 8;
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ topk_idx, int64_t a0, int64_t hi,
+                                         int (&e)[kIdBatch]) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) e[u] = topk_idx[min(a0 + 64 * u + lane, hi - 1)];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u)
+        if (a0 + 64 * u + lane >= hi) e[u] = -1;
+}
+
 // Adds the expert histogram of this wave's slice to hist[0 .. E) (hist private to the wave).
 __device__ void wave_histogram(const int32_t* __restrict__ topk_idx, int64_t lo, int64_t hi, int E, int nbits,
                                int32_t* hist) {
     const int lane = threadIdx.x & 63;
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int64_t a0 = lo; a0 < hi; a0 += 64) {
-        const int64_t a = a0 + lane;
-        const bool in = a < hi;
-        const int e = in ? topk_idx[a] : -1;
-        const bool valid = in && e >= 0 && e < E;
-        const uint32_t key = valid ? static_cast<uint32_t>(e) : (1u << nbits) - 1u;
-        const uint64_t same = same_key_lanes(key, nbits, __ballot(valid));
-        if (valid && (same & below) == 0) hist[e] += __popcll(same);
+    for (int64_t a00 = lo; a00 < hi; a00 += 64 * kIdBatch) {
+        int ev[kIdBatch];
+        load_ids(topk_idx, a00, hi, ev);
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u) {
+            if (a00 + 64 * u >= hi) break;  // uniform
+            const int e = ev[u];            // -1 past hi
+            const bool valid = e >= 0 && e < E;
+            const uint32_t key = valid ? static_cast<uint32_t>(e) : (1u << nbits) - 1u;
+            const uint64_t same = same_key_lanes(key, nbits, __ballot(valid));
+            if (valid && (same & below) == 0) hist[e] += __popcll(same);
+        }
     }
 }
 
@@ -70,7 +88,7 @@ __global__ __launch_bounds__(kRankWaves * 64) void expert_count_kernel(const int
                                                                        int nchunks, int32_t* __restrict__ count) {
     __shared__ int32_t hist[kRankWaves][kMaxExperts];
     const int w = threadIdx.x >> 6, c = blockIdx.x;
-    for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) hist[i / E][i % E] = 0;
+    for (int i = threadIdx.x; i < kRankWaves * kMaxExperts; i += blockDim.x) (&hist[0][0])[i] = 0;
     __syncthreads();
     int64_t lo, hi;
     wave_slice(n_assign, chunk, c, w, lo, hi);
@@ -96,8 +114,21 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(int32_t* __restrict__
     __shared__ int32_t wsum[1024 / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int stride = nchunks + 1;
-    const int n = E * nchunks;
-    for (int i = tid; i < n; i += 1024) cs[(i / nchunks) * stride + i % nchunks] = count[i];
+    // half-wavefront h of wave w moves row e = 2 * (16 * it + w) + h, lane & 31 = its chunk
+    const int half_row = 2 * wave + (lane >> 5), col = lane & 31;
+    for (int e0 = 0; e0 < E; e0 += 32 * kIdBatch) {  // kIdBatch loads in flight per thread
+        int32_t v[kIdBatch];
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u) {
+            const int e = min(e0 + 32 * u + half_row, E - 1);
+            v[u] = count[e * nchunks + min(col, nchunks - 1)];
+        }
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u) {
+            const int e = e0 + 32 * u + half_row;
+            if (e < E && col < nchunks) cs[e * stride + col] = v[u];
+        }
+    }
     __syncthreads();
     int32_t total = 0;
     if (tid < E)
@@ -128,7 +159,8 @@ __global__ __launch_bounds__(1024) void expert_scan_kernel(int32_t* __restrict__
         expert_offsets[E] = all;
     }
     __syncthreads();
-    for (int i = tid; i < n; i += 1024) count[i] = cs[(i / nchunks) * stride + i % nchunks];
+    for (int e = half_row; e < E; e += 32)
+        if (col < nchunks) count[e * nchunks + col] = cs[e * stride + col];
 }
 
 // One workgroup per chunk: stable ranks, row_of and row_src.
@@ -137,7 +169,7 @@ __global__ __launch_bounds__(kRankWaves * 64) void expert_rank_kernel(
     const int32_t* __restrict__ base, int32_t* __restrict__ row_of, int32_t* __restrict__ row_src) {
     __shared__ int32_t next[kRankWaves][kMaxExperts];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, c = blockIdx.x;
-    for (int i = threadIdx.x; i < kRankWaves * E; i += blockDim.x) next[i / E][i % E] = 0;
+    for (int i = threadIdx.x; i < kRankWaves * kMaxExperts; i += blockDim.x) (&next[0][0])[i] = 0;
     __syncthreads();
     int64_t lo, hi;
     wave_slice(n_assign, chunk, c, w, lo, hi);
@@ -156,21 +188,28 @@ __global__ __launch_bounds__(kRankWaves * 64) void expert_rank_kernel(
     __syncthreads();
     int32_t* nx = next[w];
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int64_t a0 = lo; a0 < hi; a0 += 64) {
-        const int64_t a = a0 + lane;
-        const bool in = a < hi;
-        const int e = in ? topk_idx[a] : -1;
-        const bool valid = in && e >= 0 && e < E;
-        const uint32_t key = valid ? static_cast<uint32_t>(e) : (1u << nbits) - 1u;
-        const uint64_t same = same_key_lanes(key, nbits, __ballot(valid));
-        int pos = -1;
-        if (valid) pos = nx[e] + static_cast<int>(__popcll(same & below));
-        // every lane has read nx[e] (one LDS instruction, in program order) before the
-        // lowest lane of each expert moves that expert's counter
-        if (valid && (same & below) == 0) nx[e] += static_cast<int>(__popcll(same));
-        if (in) {
-            row_of[a] = pos;
-            if (pos >= 0) row_src[pos] = static_cast<int32_t>(a / k);
+    for (int64_t a00 = lo; a00 < hi; a00 += 64 * kIdBatch) {
+        int ev[kIdBatch];
+        load_ids(topk_idx, a00, hi, ev);
+#pragma unroll
+        for (int u = 0; u < kIdBatch; ++u) {
+            const int64_t a0 = a00 + 64 * u;
+            if (a0 >= hi) break;  // uniform
+            const int64_t a = a0 + lane;
+            const bool in = a < hi;
+            const int e = ev[u];  // -1 past hi
+            const bool valid = e >= 0 && e < E;
+            const uint32_t key = valid ? static_cast<uint32_t>(e) : (1u << nbits) - 1u;
+            const uint64_t same = same_key_lanes(key, nbits, __ballot(valid));
+            int pos = -1;
+            if (valid) pos = nx[e] + static_cast<int>(__popcll(same & below));
+            // every lane has read nx[e] (one LDS instruction, in program order) before the
+            // lowest lane of each expert moves that expert's counter
+            if (valid && (same & below) == 0) nx[e] += static_cast<int>(__popcll(same));
+            if (in) {
+                row_of[a] = pos;
+                if (pos >= 0) row_src[pos] = static_cast<int32_t>(static_cast<uint32_t>(a) / static_cast<uint32_t>(k));
+            }
         }
     }
 }
