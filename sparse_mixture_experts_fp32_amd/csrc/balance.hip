@@ -46,11 +46,11 @@ __global__ __launch_bounds__(256) void qb_select_kernel(const float* __restrict_
     float v[NPER], b[NPER];
     load_row_strided<NPER>(row, E, 0.f, v);
     load_row_strided<NPER>(bias, E, 0.f, b);
-    uint32_t vk[NPER];
+    float sc[NPER];
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) vk[i] = order_key(v[i] + b[i]);
+    for (int i = 0; i < NPER; ++i) sc[i] = v[i] + b[i];
     // lane j <= k: the j-th largest biased key (lane k: the cutoff)
-    const uint64_t best = select_top<NPER>(vk, E, k + 1, sel[threadIdx.x >> 6]);
+    const uint64_t best = select_top<NPER>(sc, E, k + 1, sel[threadIdx.x >> 6]);
     const int my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
     const float my_score = key_value(static_cast<uint32_t>(best >> 32));
     const bool chosen = lane < k;

@@ -242,11 +242,8 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 
     float v[NPER];
     load_row_strided<NPER>(row, E, 0.f, v);
-    uint32_t vk[NPER];
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) vk[i] = order_key(v[i]);
     // lane j < k: the j-th largest key
-    const uint64_t best = select_top<NPER>(vk, E, k, sel[threadIdx.x >> 6]);
+    const uint64_t best = select_top<NPER>(v, E, k, sel[threadIdx.x >> 6]);
     const int my_id = static_cast<int>(0xffffffffu - static_cast<uint32_t>(best));
     const float my_val = key_value(static_cast<uint32_t>(best >> 32));
     const float top = __shfl(my_val, 0, kWave);

@@ -1,23 +1,28 @@
-// Wavefront top-K of up to 64 * NPER keys (one wavefront per token).
+// Wavefront top-K of up to 64 * NPER scores (one wavefront per token).
 //
 // Element i of lane l is expert e = l + 64 i (valid when e < E). Its 64-bit key
-// is (value key << 32) | ~e, with the value key from order_key, so keys are
-// distinct and the largest key is the largest value with ties to the lower id.
-// select_top leaves, in lane j < K, the j-th largest key.
+// is (order_key(score) << 32) | ~e, so keys are distinct and the largest key is
+// the largest score with ties to the lower id (-0 ties +0, NaN below every
+// number). select_top leaves, in lane j < K, the j-th largest key.
 //
 // Instead of K rounds of "local maximum over NPER keys, wavefront maximum,
 // clear the winner" (K * NPER work per lane), a threshold prunes first:
 //   1. tau = the K-th largest of the 64 lanes' largest value keys, found bit
 //      by bit with ballots. At least K keys have a value key >= tau (those
 //      lane maxima), so every one of the K largest keys has value key >= tau.
-//   2. The keys with value key >= tau (the candidates) are compacted into a
-//      64-entry LDS array of the wavefront: the ballot of each element index is
-//      the write mask, and each writing lane's slot is the count of writing
+//   2. The elements with value key >= tau (the candidates) are compacted into
+//      a 64-entry LDS array of the wavefront: the ballot of each element index
+//      is the write mask, and each writing lane's slot is the count of writing
 //      lanes below it (mbcnt).
 //   3. Each candidate counts the candidates above it (its rank) by reading the
 //      array back (one broadcast read per candidate); the candidate of rank j
 //      is written to entry j of a second array and lane j reads it.
-// More than 64 candidates (massive ties) fall back to the round-based selection.
+// Steps 1 and 2 compare the scores as floats: order_key is monotone, tau is the
+// key of one lane's maximum, a non-NaN number f whenever tau != 0, and then
+// order_key(s) >= tau exactly when s >= f (denormals are kept, -0 == +0, NaN
+// fails both). Only the candidates get their 64-bit keys. tau == 0 (NaN or
+// padding among the lane maxima) and more than 64 candidates (massive ties)
+// take the round-based selection on full keys.
 #pragma once
 
 #include "device_common.h"
@@ -43,42 +48,55 @@ __device__ __forceinline__ void load_row_strided(const float* __restrict__ row, 
 
 constexpr int kSelectLds = 128;  // uint64 entries of LDS per wavefront (two arrays of 64)
 
-// vk[i]: value key of element i (order_key of its score); E: valid elements
-// (64 (NPER - 1) < E <= 64 NPER); K <= E.
+// v[i]: score of element i; E: valid elements (64 (NPER - 1) < E <= 64 NPER); K <= E.
 template <int NPER>
-__device__ __forceinline__ uint64_t select_top(const uint32_t (&vk)[NPER], int E, int K, uint64_t* lds) {
+__device__ __forceinline__ uint64_t select_top(const float (&v)[NPER], int E, int K, uint64_t* lds) {
     const int lane = threadIdx.x & 63;
     const bool last_on = lane + 64 * (NPER - 1) < E;  // only the last element can be padding
-    auto key_of = [&](int i) {
-        return (static_cast<uint64_t>(vk[i]) << 32) | (0xffffffffu - static_cast<uint32_t>(lane + 64 * i));
+    auto key_of = [](float x, uint32_t id) {
+        return (static_cast<uint64_t>(order_key(x)) << 32) | (0xffffffffu - id);
     };
-    // 1. tau over the lanes' largest value keys (padding counts as 0)
-    uint32_t m = last_on ? vk[NPER - 1] : 0u;
+    // 1. tau over the lanes' largest value keys (padding and NaN count as 0)
+    float mf = last_on ? v[NPER - 1] : __uint_as_float(0x7fc00000u);
 #pragma unroll
-    for (int i = 0; i < NPER - 1; ++i) m = max(m, vk[i]);
+    for (int i = 0; i < NPER - 1; ++i) mf = fmaxf(mf, v[i]);  // a NaN operand loses
+    uint32_t m = order_key(mf);
+    asm volatile("" : "+v"(m));  // materialise m once (else its NaN select is re-evaluated in every step below)
     uint32_t tau = 0u;
     for (int b = 31; b >= 0; --b) {
         const uint32_t cand = tau | (1u << b);
         if (__popcll(__ballot(m >= cand)) >= K) tau = cand;
     }
-    // 2. candidates, compacted in (element, lane) order while they are counted
-    int total = 0;
+    // 2. candidates, compacted as (score bits, id) in (element, lane) order while they are counted
+    int total = 65;
+    if (tau != 0u) {
+        const float f = key_value(tau);
+        total = 0;
 #pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-        const bool c = vk[i] >= tau && (i < NPER - 1 || last_on);
-        const uint64_t bal = __ballot(c);
-        if (c && total + __popcll(bal) <= 64) {
-            const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                                             __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
-            lds[total + static_cast<int>(below)] = key_of(i);
+        for (int i = 0; i < NPER; ++i) {
+            const bool c = v[i] >= f && (i < NPER - 1 || last_on);
+            const uint64_t bal = __ballot(c);
+            if (c && total + __popcll(bal) <= 64) {
+                const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u));
+                lds[total + static_cast<int>(below)] =
+                    (static_cast<uint64_t>(__float_as_uint(v[i])) << 32) | static_cast<uint32_t>(lane + 64 * i);
+            }
+            total += __popcll(bal);
         }
-        total += __popcll(bal);
     }
     uint64_t mine = 0ull;
     if (total <= 64) {
         __builtin_amdgcn_wave_barrier();
-        // 3. ranks, then the candidates in rank order
-        const uint64_t my = lane < total ? lds[lane] : 0ull;
+        // 3. each candidate's key into its own slot, then ranks, then the candidates in rank order
+        uint64_t my = 0ull;
+        if (lane < total) {
+            const uint64_t p = lds[lane];
+            my = key_of(__uint_as_float(static_cast<uint32_t>(p >> 32)), static_cast<uint32_t>(p));
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane < total) lds[lane] = my;
+        __builtin_amdgcn_wave_barrier();
         int rank = 0;
         for (int c = 0; c < total; ++c) rank += lds[c] > my ? 1 : 0;
         __builtin_amdgcn_wave_barrier();
@@ -88,7 +106,8 @@ __device__ __forceinline__ uint64_t select_top(const uint32_t (&vk)[NPER], int E
     } else {
         uint64_t key[NPER];
 #pragma unroll
-        for (int i = 0; i < NPER; ++i) key[i] = (i < NPER - 1 || last_on) ? key_of(i) : 0ull;
+        for (int i = 0; i < NPER; ++i)
+            key[i] = (i < NPER - 1 || last_on) ? key_of(v[i], static_cast<uint32_t>(lane + 64 * i)) : 0ull;
         for (int j = 0; j < K; ++j) {
             uint64_t best = key[0];
 #pragma unroll
