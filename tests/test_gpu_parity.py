@@ -63,6 +63,41 @@ def test_topk_softmax_planted_ties(dev, moe, T, E, k):
     assert list(gi[0]) == list(range(k)), "all-zero row must pick experts 0..k-1"
 
 
+def _zero_threshold_logits(E):
+    """Rows whose k-th largest lane maximum (lane = id % 64) is exactly 0 or a negative
+    denormal, with -0.0, +0.0 and denormals of both signs around it: the selection must
+    tie -0 with +0 (lower id first) and keep a denormal apart from 0."""
+    den = np.float32(1e-40)       # a float32 denormal
+    tiny = np.float32(1.4e-45)    # the smallest one
+    rows = []
+    a = np.full(E, -1.0, np.float32)
+    a[0:20] = 0.0                 # 20 lanes whose maximum is 0 ...
+    a[1:20:2] = -0.0              # ... half of them -0
+    a[64:84:3] = -0.0             # more zeros in the same lanes (higher ids)
+    a[20:25] = den                # 5 lanes above 0
+    a[30:40] = -den               # negative denormals: below every zero
+    rows.append(a)
+    b = np.full(E, -1.0, np.float32)
+    b[0:10] = 0.0                 # 10 lanes at 0 or above ...
+    b[3] = tiny
+    b[5] = -0.0
+    b[10:22] = -tiny              # ... then 12 lanes at the largest negative denormal
+    b[64 + 10:64 + 14] = -tiny    # ties on it in those lanes, higher ids
+    b[22:30] = -den
+    rows.append(b)
+    c = -np.abs(a)                # all non-positive: zeros of both signs are the largest
+    rows.append(c)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("E,k", [(896, 16), (128, 8), (100, 12)])
+def test_topk_threshold_at_zero_and_denormals(dev, moe, E, k):
+    L = _zero_threshold_logits(E)
+    idx, w = moe.moe_topk_softmax(torch.from_numpy(L).to(dev), k)
+    _sync()
+    gu.check_route(torch.from_numpy(L), idx, w, k)
+
+
 def test_topk_nan_rows_still_give_distinct_ids(dev, moe):
     E, k = 96, 8
     L = np.random.default_rng(0).standard_normal((6, E)).astype(np.float32)
