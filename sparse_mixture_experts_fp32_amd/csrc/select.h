@@ -8,8 +8,9 @@
 // Instead of K rounds of "local maximum over NPER keys, wavefront maximum,
 // clear the winner" (K * NPER work per lane), a threshold prunes first:
 //   1. tau = the K-th largest of the 64 lanes' largest value keys, found bit
-//      by bit with ballots. At least K keys have a value key >= tau (those
-//      lane maxima), so every one of the K largest keys has value key >= tau.
+//      by bit with ballots down to its upper 16 bits (so rounded down). At
+//      least K keys have a value key >= tau (those lane maxima), so every one
+//      of the K largest keys has value key >= tau.
 //   2. The elements with value key >= tau (the candidates) are compacted into
 //      a 64-entry LDS array of the wavefront: the ballot of each element index
 //      is the write mask, and each writing lane's slot is the count of writing
@@ -17,12 +18,15 @@
 //   3. Each candidate counts the candidates above it (its rank) by reading the
 //      array back (one broadcast read per candidate); the candidate of rank j
 //      is written to entry j of a second array and lane j reads it.
-// Steps 1 and 2 compare the scores as floats: order_key is monotone, tau is the
-// key of one lane's maximum, a non-NaN number f whenever tau != 0, and then
-// order_key(s) >= tau exactly when s >= f (denormals are kept, -0 == +0, NaN
-// fails both). Only the candidates get their 64-bit keys. tau == 0 (NaN or
-// padding among the lane maxima) and more than 64 candidates (massive ties)
-// take the round-based selection on full keys.
+// Step 2 compares the scores as floats: order_key is monotone and maps the
+// non-NaN floats (-0 and +0 to one key) one to one onto the keys it produces, so
+// for a threshold f = key_value(tau) that is a number, order_key(s) >= tau
+// exactly when s >= f (denormals are kept, -0 == +0, NaN fails both; tau =
+// 0x7fffffff gives f = -0, and both sides then admit exactly s >= 0). Only the
+// candidates get their 64-bit keys. A zero tau (NaN or padding among the lane
+// maxima), a threshold that is not a number (a k-th lane maximum of -inf) and
+// more than 64 candidates (massive ties) take the round-based selection on full
+// keys.
 #pragma once
 
 #include "device_common.h"
@@ -47,6 +51,11 @@ __device__ __forceinline__ void load_row_strided(const float* __restrict__ row, 
 }
 
 constexpr int kSelectLds = 128;  // uint64 entries of LDS per wavefront (two arrays of 64)
+// The bisection for tau stops above this many low key bits: tau is then at most
+// the k-th largest lane maximum and within 2^-7 of it in relative terms, still a
+// valid threshold (at least K value keys reach it), which admits a few more
+// candidates in exchange for half the serial ballot steps.
+constexpr int kSelectLowBits = 16;
 
 // v[i]: score of element i; E: valid elements (64 (NPER - 1) < E <= 64 NPER); K <= E.
 template <int NPER>
@@ -63,14 +72,14 @@ __device__ __forceinline__ uint64_t select_top(const float (&v)[NPER], int E, in
     uint32_t m = order_key(mf);
     asm volatile("" : "+v"(m));  // materialise m once (else its NaN select is re-evaluated in every step below)
     uint32_t tau = 0u;
-    for (int b = 31; b >= 0; --b) {
+    for (int b = 31; b >= kSelectLowBits; --b) {
         const uint32_t cand = tau | (1u << b);
         if (__popcll(__ballot(m >= cand)) >= K) tau = cand;
     }
     // 2. candidates, compacted as (score bits, id) in (element, lane) order while they are counted
     int total = 65;
-    if (tau != 0u) {
-        const float f = key_value(tau);
+    const float f = key_value(tau);
+    if (tau != 0u && f == f) {
         total = 0;
 #pragma unroll
         for (int i = 0; i < NPER; ++i) {
