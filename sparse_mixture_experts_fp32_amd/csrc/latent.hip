@@ -12,23 +12,26 @@ namespace moe {
 
 // ----------------------------------------------------- combine + RMSNorm
 //
-// One wavefront per token. Lane l owns the float4 chunks c = l, l + 64, ... of
-// the latent row (NC of them, kept in registers): it forms
-// u = sum_{j<k} w[t, j] * Y[row_of[t, j]] in slot order (as moe_combine does),
-// then the wavefront sums u^2 (each lane over its chunks in order, then a
-// butterfly), and writes bf16(u * (1 / sqrt(mean u^2 + eps)) * g). u itself is
-// written as well when u_out is given.
+// One workgroup of four wavefronts per token. Thread i owns the float4 chunks
+// c = i, i + 256, ... of the latent row (NCT of them): it forms
+// u = sum_{j<k} w[t, j] * Y[row_of[t, j]] in slot order (as moe_combine does, so
+// u is bitwise moe_combine's row), issuing the loads of kSl slots before their
+// multiply-adds (Y rows are read once, so non-temporally). The sum of u^2 runs
+// over each thread's chunks in order, a wavefront butterfly, then the four
+// wavefront sums in order (the same value in every thread); the kernel writes
+// bf16(u * (1 / sqrt(mean u^2 + eps)) * g), and u itself when u_out is given.
 
-template <int NC>
+template <int NCT, int kSl>
 __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float* __restrict__ Y, int l,
                                                               const int32_t* __restrict__ row_of,
                                                               const float* __restrict__ w, int64_t T, int k,
                                                               int64_t n_rows, const float* __restrict__ gain,
                                                               float eps, float* __restrict__ u_out,
                                                               uint16_t* __restrict__ r_out) {
-    const int lane = threadIdx.x & 63;
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;  // whole wavefront
+    __shared__ float wave_ss[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t t = blockIdx.x;
+    if (t >= T) return;  // whole workgroup
     int my_row = -1;
     float my_w = 0.f;
     if (lane < k) {
@@ -37,43 +40,60 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float* __res
         if (my_row < 0 || my_row >= n_rows) my_row = -1;
     }
     const int nchunk = l / 4;
-    float4 u[NC];
+    f32x4 u[NCT];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) u[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int r = __shfl(my_row, j, 64);
-        const float wj = __shfl(my_w, j, 64);
-        if (r < 0) continue;  // uniform
-        const float4* yrow = reinterpret_cast<const float4*>(Y + static_cast<int64_t>(r) * l);
+    for (int i = 0; i < NCT; ++i) u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += kSl) {
+        f32x4 v[kSl][NCT];
+        float wj[kSl];
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
-            const int c = lane + 64 * i;
-            if (c < nchunk) {
-                const float4 v = yrow[c];
-                u[i].x = fmaf(wj, v.x, u[i].x);
-                u[i].y = fmaf(wj, v.y, u[i].y);
-                u[i].z = fmaf(wj, v.z, u[i].z);
-                u[i].w = fmaf(wj, v.w, u[i].w);
+        for (int s = 0; s < kSl; ++s) {  // all loads of this group first
+            const int j = j0 + s;
+            const int r = __shfl(my_row, j & 63, kWave);
+            wj[s] = __shfl(my_w, j & 63, kWave);
+            const bool on = j < k && r >= 0;
+            const f32x4* yrow = reinterpret_cast<const f32x4*>(Y + static_cast<int64_t>(on ? r : 0) * l);
+#pragma unroll
+            for (int i = 0; i < NCT; ++i) {
+                const int c = tid + 256 * i;
+                v[s][i] = (on && c < nchunk) ? __builtin_nontemporal_load(yrow + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if (!on) wj[s] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kSl; ++s) {  // then the sums, in slot order
+            if (j0 + s >= k) break;      // uniform
+            const int r = __shfl(my_row, (j0 + s) & 63, kWave);
+            if (r < 0) continue;         // uniform: a skipped slot adds nothing
+#pragma unroll
+            for (int i = 0; i < NCT; ++i) {
+                u[i].x = fmaf(wj[s], v[s][i].x, u[i].x);
+                u[i].y = fmaf(wj[s], v[s][i].y, u[i].y);
+                u[i].z = fmaf(wj[s], v[s][i].z, u[i].z);
+                u[i].w = fmaf(wj[s], v[s][i].w, u[i].w);
             }
         }
     }
-    float ss = 0.f;
+    float ss = 0.f;  // chunks past the row end hold zeros
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
+    for (int i = 0; i < NCT; ++i) {
         ss = fmaf(u[i].x, u[i].x, ss);
         ss = fmaf(u[i].y, u[i].y, ss);
         ss = fmaf(u[i].z, u[i].z, ss);
         ss = fmaf(u[i].w, u[i].w, ss);
     }
     ss = wave_sum_f32(ss);
-    const float rs = 1.0f / sqrtf(ss / static_cast<float>(l) + eps);
-    const float4* g4 = reinterpret_cast<const float4*>(gain);
+    if (lane == 0) wave_ss[wave] = ss;
+    __syncthreads();
+    const float total = ((wave_ss[0] + wave_ss[1]) + wave_ss[2]) + wave_ss[3];
+    const float rs = 1.0f / sqrtf(total / static_cast<float>(l) + eps);
+    const f32x4* g4 = reinterpret_cast<const f32x4*>(gain);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int c = lane + 64 * i;
+    for (int i = 0; i < NCT; ++i) {
+        const int c = tid + 256 * i;
         if (c >= nchunk) continue;
-        const float4 g = g4[c];
-        if (u_out != nullptr) reinterpret_cast<float4*>(u_out + t * l)[c] = u[i];
+        const f32x4 g = g4[c];
+        if (u_out != nullptr) reinterpret_cast<f32x4*>(u_out + t * l)[c] = u[i];
         const uint32_t lo = f32_to_bf16_bits(u[i].x * rs * g.x) | (uint32_t(f32_to_bf16_bits(u[i].y * rs * g.y)) << 16);
         const uint32_t hi = f32_to_bf16_bits(u[i].z * rs * g.z) | (uint32_t(f32_to_bf16_bits(u[i].w * rs * g.w)) << 16);
         reinterpret_cast<uint2*>(r_out + t * l)[c] = make_uint2(lo, hi);
@@ -123,25 +143,20 @@ int combine_rmsnorm_max_width() { return 64 * 4 * 32; }
 hipError_t launch_combine_rmsnorm(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T, int l,
                                   int k, int64_t n_rows, const float* gain, float eps, float* u_out,
                                   uint16_t* r_out, hipStream_t stream) {
-    const int nc = (l / 4 + 63) / 64;
-    dim3 grid(static_cast<unsigned>((T + 3) / 4));
-#define MOE_CR(N)                                                                                               \
-    hipLaunchKernelGGL(combine_rmsnorm_kernel<N>, grid, dim3(256), 0, stream, y_rows, l, row_of, topk_w, T, k, \
+    if (T <= 0) return hipSuccess;
+    const int nct = (l / 4 + 255) / 256;  // float4 chunks per thread
+    dim3 grid(static_cast<unsigned>(T));
+#define MOE_CR(N, S)                                                                                               \
+    hipLaunchKernelGGL((combine_rmsnorm_kernel<N, S>), grid, dim3(256), 0, stream, y_rows, l, row_of, topk_w, T, k, \
                        n_rows, gain, eps, u_out, r_out)
-    if (nc <= 2) {
-        MOE_CR(2);
-    } else if (nc <= 4) {
-        MOE_CR(4);
-    } else if (nc <= 8) {
-        MOE_CR(8);
-    } else if (nc <= 14) {
-        MOE_CR(14);
-    } else if (nc <= 16) {
-        MOE_CR(16);
-    } else if (nc <= 24) {
-        MOE_CR(24);
-    } else if (nc <= 32) {
-        MOE_CR(32);
+    if (nct <= 1) {
+        MOE_CR(1, 8);
+    } else if (nct <= 2) {
+        MOE_CR(2, 4);
+    } else if (nct <= 4) {
+        MOE_CR(4, 4);
+    } else if (nct <= 8) {
+        MOE_CR(8, 2);
     } else {
         return hipErrorInvalidValue;
     }

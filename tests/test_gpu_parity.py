@@ -98,6 +98,22 @@ def test_topk_threshold_at_zero_and_denormals(dev, moe, E, k):
     gu.check_route(torch.from_numpy(L), idx, w, k)
 
 
+@pytest.mark.parametrize("E,k", [(896, 16), (130, 8)])
+def test_topk_rows_mostly_minus_inf(dev, moe, E, k):
+    """Fewer finite scores than k: the k-th lane maximum is -inf, and the -inf ties go to the lower ids."""
+    r = np.random.default_rng(E + k)
+    L = np.full((4, E), -np.inf, np.float32)
+    for t, n_finite in enumerate([0, 1, k // 2, k - 1]):
+        pos = r.choice(E, size=n_finite, replace=False)
+        L[t, pos] = r.standard_normal(n_finite).astype(np.float32)
+    idx, w = moe.moe_topk_softmax(torch.from_numpy(L).to(dev), k)
+    _sync()
+    gi = idx.cpu().numpy()
+    with np.errstate(invalid="ignore"):  # the all -inf row has no defined softmax; only ids are compared
+        idx_ref, _, _ = orc.route(L.astype(np.float64), k)
+    assert np.array_equal(gi, idx_ref), (gi, idx_ref)
+
+
 def test_topk_nan_rows_still_give_distinct_ids(dev, moe):
     E, k = 96, 8
     L = np.random.default_rng(0).standard_normal((6, E)).astype(np.float32)
