@@ -75,6 +75,7 @@ hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const floa
                           int d, int k, int64_t n_rows, float* out, hipStream_t stream) {
     if (T <= 0) return hipSuccess;
     const int64_t items = T * ((d + kBlockCols - 1) / kBlockCols);
+    if ((items + 3) / 4 > INT32_MAX) return hipErrorInvalidValue;  // beyond one launch's grid
     hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, stream, y_rows,
                        d, row_of, topk_w, T, k, n_rows, out);
     return hipGetLastError();

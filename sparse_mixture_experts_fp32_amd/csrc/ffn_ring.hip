@@ -168,10 +168,10 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
                 uint16_t* crow = static_cast<uint16_t*>(Cout) + (row0 + r) * N + n_out + frag_row;
 #pragma unroll
                 for (int j = 0; j < kRNB; ++j) crow[16 * j] = f32_to_bf16_bits(acc[j][i][q]);
-            } else {  // Y row: float32
+            } else {  // Y row: float32, written once and read back only by the combine: non-temporal
                 float* crow = static_cast<float*>(Cout) + (row0 + r) * N + n_out + frag_row;
 #pragma unroll
-                for (int j = 0; j < kRNB; ++j) crow[16 * j] = acc[j][i][q];
+                for (int j = 0; j < kRNB; ++j) __builtin_nontemporal_store(acc[j][i][q], crow + 16 * j);
             }
         }
     }
