@@ -285,10 +285,10 @@ __device__ __forceinline__ void ffn_tile(uint16_t* sA, const uint16_t* __restric
                 uint16_t* crow = static_cast<uint16_t*>(Cout) + (row0 + r) * N + n_wave + frag_row;
 #pragma unroll
                 for (int b = 0; b < kNB; ++b) crow[16 * b] = f32_to_bf16_bits(acc[b][i][q]);
-            } else {             // Y row: float32
+            } else {             // Y row: float32, read back only by a later pass over many other bytes
                 float* crow = static_cast<float*>(Cout) + (row0 + r) * N + n_wave + frag_row;
 #pragma unroll
-                for (int b = 0; b < kNB; ++b) crow[16 * b] = acc[b][i][q];
+                for (int b = 0; b < kNB; ++b) __builtin_nontemporal_store(acc[b][i][q], crow + 16 * b);
             }
         }
     }

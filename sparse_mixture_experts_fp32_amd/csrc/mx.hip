@@ -313,7 +313,7 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
                 for (int c = 0; c < kMxNB / 2; ++c) crow[16 * c] = acc[c][i][qq];
             } else {
 #pragma unroll
-                for (int b = 0; b < kMxNB; ++b) crow[16 * b] = acc[b][i][qq];
+                for (int b = 0; b < kMxNB; ++b) __builtin_nontemporal_store(acc[b][i][qq], crow + 16 * b);  // Y rows
             }
         }
     }
