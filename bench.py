@@ -116,9 +116,10 @@ class Layer:
 
 
 def time_hbm_kernels(layer, reps):
-    """Mean time of the routing top-k, permute and combine calls, each on its own, on the step's
-    buffers (HIP events on the layer's stream; each rewrites the values the step wrote), and the
-    rate of each in algorithmic bytes: every input read once, every output written once."""
+    """Mean time of the routing top-k, permute (with and without the x_perm gather) and combine
+    calls, each on its own, on the step's buffers (HIP events on the layer's stream; each rewrites
+    the values the step wrote), and the rate of each in algorithmic bytes: every input read once,
+    every output written once."""
     import torch
     L, P, sh, sp, c = layer.lib.lib, layer.P, layer.sh, layer.sp, layer.lib.check
     cfg = layer.cfg
@@ -132,6 +133,13 @@ def time_hbm_kernels(layer, reps):
         "combine": (lambda: c(L.moe_combine(sh, P(layer.y_rows), P(layer.row_of), P(layer.w), P(layer.out), sp)),
                     4.0 * T * k * d + 8.0 * T * k + 4.0 * T * d, "hbm"),
     }
+    # the dispatch gather as moe_permute's optional x_perm output (the layer fuses it into the gate/up pass):
+    # the permute's bytes plus x read once and x_perm written once
+    x_perm = torch.empty(T * k, d, dtype=torch.bfloat16, device=layer.dev)
+    calls["permute_gather"] = (
+        lambda: c(L.moe_permute(sh, P(layer.inp.x), P(layer.idx), P(layer.offsets), P(layer.row_of),
+                                P(layer.row_src), P(x_perm), P(layer.ws_perm), layer.ws_perm.numel(), sp)),
+        4.0 * T * k + 4.0 * (E + 1) + 8.0 * T * k + 2.0 * T * d + 2.0 * T * k * d, "hbm")
     out = {"reps": reps}
     for name, (call, nbytes, bound) in calls.items():
         for _ in range(3):

@@ -214,20 +214,27 @@ __global__ __launch_bounds__(kRankWaves * 64) void expert_rank_kernel(
     }
 }
 
-// x_perm[r] = x[row_src[r]]: one wavefront copies one row, 16 bytes per lane.
-// Rows past expert_offsets[E] (only when some ids were out of range) are left alone.
+// x_perm[r] = x[row_src[r]]: one wavefront copies one 512-element (1 KiB) block of
+// one row, 16 bytes per lane, so there are many small work items and each lane
+// makes a single load and store. x_perm is written once and read by a later
+// pass over many other bytes, so it is stored non-temporally. Rows past
+// expert_offsets[E] (only when some ids were out of range) are left alone.
+constexpr int kGatherCols = 512;  // bf16 elements per work item
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x, int64_t T, int d,
                                                           const int32_t* __restrict__ row_src,
                                                           const int32_t* __restrict__ n_valid,
                                                           int64_t n_rows, uint16_t* __restrict__ x_perm) {
     const int lane = threadIdx.x & 63;
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int nblk = (d + kGatherCols - 1) / kGatherCols;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int64_t r = item / nblk;
     if (r >= n_rows || r >= *n_valid) return;
     const int src = row_src[r];
     if (src < 0 || src >= T) return;
-    const uint4* s = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(src) * d);
-    uint4* o = reinterpret_cast<uint4*>(x_perm + r * d);
-    for (int c = lane; c < d / 8; c += 64) o[c] = s[c];
+    const int c = static_cast<int>(item - r * nblk) * (kGatherCols / 8) + lane;  // 16-byte chunk of the row
+    if (c >= d / 8) return;
+    const u32x4 v = reinterpret_cast<const u32x4*>(x + static_cast<int64_t>(src) * d)[c];
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(x_perm + r * d) + c);
 }
 
 __global__ void zero_i32_kernel(int32_t* __restrict__ p, int n) {
@@ -274,9 +281,12 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
     hipLaunchKernelGGL(expert_scan_kernel, dim3(1), dim3(1024), 0, stream, count_ws, E, nchunks, expert_offsets);
     hipLaunchKernelGGL(expert_rank_kernel, dim3(nchunks), dim3(kRankWaves * 64), 0, stream, topk_idx, n, k, E, nbits,
                        chunk, nchunks, count_ws, row_of, row_src);
-    if (x_perm != nullptr)
-        hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>((n + 3) / 4)), dim3(256), 0, stream,
+    if (x_perm != nullptr) {
+        const int64_t items = n * ((d + kGatherCols - 1) / kGatherCols);
+        if ((items + 3) / 4 > INT32_MAX) return hipErrorInvalidValue;  // beyond one launch's grid
+        hipLaunchKernelGGL(gather_rows_kernel, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, stream,
                            x, T, d, row_src, expert_offsets + E, n, x_perm);
+    }
     return hipGetLastError();
 }
 
