@@ -220,8 +220,9 @@ __global__ __launch_bounds__(256) void aux_partial_kernel(const float* __restric
             s += v[i];
         }
         s = wave_sum_f32(s);
+        const float inv = 1.0f / s;  // one division per token, then a fused multiply-add per expert
 #pragma unroll
-        for (int i = 0; i < NPER; ++i) acc[i] += v[i] / s;
+        for (int i = 0; i < NPER; ++i) acc[i] = fmaf(v[i], inv, acc[i]);
     }
 #pragma unroll
     for (int i = 0; i < NPER; ++i) red[w][i * 64 + lane] = acc[i];

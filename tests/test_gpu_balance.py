@@ -8,9 +8,10 @@ Tolerances:
     operation by operation, on the same integer counts, then round once);
   * QB weights: |dw| <= 1e-5 (same device logits on both sides);
   * expert mean probabilities: |dm_e| <= 1e-5 m_e. Each device probability is
-    expf, a float32 sum of at most 16 * 64 exponentials and one division
-    (relative error below 2e-6); the float32 partial sums over 16 tokens and
-    4 wavefronts add below 2e-6 more (all terms positive); float64 after that;
+    expf, a float32 sum of at most 16 * 64 exponentials, one reciprocal of that
+    sum and one fused multiply-add into the running sum (relative error below
+    2e-6); the float32 partial sums over 16 tokens and 4 wavefronts add below
+    2e-6 more (all terms positive); float64 after that;
   * aux loss: it moves by sum_e (2 |m_e - 1/E| d_e + d_e^2) for errors d_e of
     the means, plus its own float32 rounding, so
     |dL| <= sum_e (2 |m_e - 1/E| d_e + d_e^2) + 2^-23 L with d_e = 1e-5 m_e.
