@@ -305,8 +305,10 @@ hipError_t launch_qb_histogram(const float* logits, const float* alpha, int64_t 
     constexpr int kLdsInts = kHistLdsBytes / sizeof(int32_t);
     const int se = n_bins * 32 <= kLdsInts ? 32 : (n_bins * 16 <= kLdsInts ? 16 : 8);
     const int nslab = (E + se - 1) / se;
-    // about two blocks of kHistThreads per compute unit, at least 64 tokens each
-    const int64_t want = std::max<int64_t>(1, 512 / nslab);
+    // one block per compute unit (its LDS histogram fills most of the CU's LDS), at least 64 tokens each:
+    // every block ends by adding its non-zero bins to the global histogram with atomics, so fewer,
+    // larger token ranges flush fewer bins
+    const int64_t want = std::max<int64_t>(1, 256 / nslab);
     const int64_t splits = std::max<int64_t>(1, std::min<int64_t>(want, (T + 63) / 64));
     const int64_t per = (T + splits - 1) / splits;
     const int64_t nblk = static_cast<int64_t>(nslab) * ((T + per - 1) / per);
