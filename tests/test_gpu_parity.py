@@ -199,6 +199,18 @@ def test_permute_vs_oracle(dev, moe, T, E, k, skew):
     assert torch.equal(x_perm.cpu(), x[torch.from_numpy(rs)]), "x_perm is not x[row_src]"
 
 
+@pytest.mark.parametrize("d", [640, 1152])
+def test_permute_gather_rows_spanning_blocks(dev, moe, d):
+    """x_perm rows wider than one 512-element gather block, with a partial last block."""
+    T, E, k = 77, 9, 3
+    idx = _random_idx(T, E, k, seed=d)
+    x = torch.randn(T, d).to(torch.bfloat16)
+    off, row_of, row_src, x_perm = moe.moe_permute(x.to(dev), torch.from_numpy(idx).to(dev), E)
+    _sync()
+    _, _, rs = gu.check_permutation(off, row_of, row_src, idx, E)
+    assert torch.equal(x_perm.cpu(), x[torch.from_numpy(rs)]), "x_perm is not x[row_src]"
+
+
 def test_permute_skips_out_of_range_ids(dev, moe):
     T, E, k, d = 40, 6, 2, 128
     idx = _random_idx(T, E, k, seed=3)
