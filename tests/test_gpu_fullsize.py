@@ -1,9 +1,10 @@
-"""GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (one moe_forward call). The oracle checks what it can compute
-in seconds: gate logits of sampled tokens, every routing id and weight, the
-whole permutation, sampled x_perm rows, every H and Y row of two experts (a
-sample of rows for a very large expert), and the layer output of sampled
-tokens computed one by one through their own experts."""
+"""GPU parity at the full workload sizes (one moe_forward call). The oracle
+checks what it can compute in seconds: gate logits of sampled tokens, every
+routing id and weight, the whole permutation, sampled x_perm rows, every H and
+Y row of two experts (a sample of rows for a very large expert), and the layer
+output of sampled tokens computed one by one through their own experts. The
+forward on packed expert weights, the configuration the benchmark times, must
+then give the same output bit for bit."""
 import sys
 
 import numpy as np
@@ -76,5 +77,13 @@ def test_full_size_layer(moe, name):
                       gu.LazyExperts(inp.w_down), cfg.k, logits=logits[toks])
     max_rel, mean_abs = gu.check_layer(out[torch.from_numpy(toks).to(dev)].cpu(), ref["out"])
     print(f"[full-size] {name}: sampled out max rel {max_rel:.2e}, mean abs {mean_abs:.2e}", flush=True)
-    del fwd, out, inp
+    del fwd
+    # the benchmarked configuration: packed expert weights, the same output bit for bit
+    packed = [moe.moe_pack_weights(w) for w in (inp.w_gate, inp.w_up, inp.w_down)]
+    out_p = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev, packed=True)(inp.x, inp.w_router,
+                                                                                inp.router_bias, *packed)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, out), "packed-weight forward differs from the row-major forward"
+    print(f"[full-size] {name}: packed-weight forward equal bit for bit", flush=True)
+    del packed, out_p, out, inp
     torch.cuda.empty_cache()
