@@ -13,7 +13,9 @@ HIP events on that stream time each GEMM pass inside every timed step.
 
 Prints one JSON line: whole-layer tokens/s, the grouped GEMM's TFLOP/s and
 MFMA fraction, the roofline of the dominant kernel (the gate/up pass) and the
-CPU oracle's rate on a bounded sample of the same workload. The "balance"
+CPU oracle's rate on a bounded sample of the same workload. The "hbm_kernels"
+object times the top-k, the permute (with and without the x_perm gather) and
+the combine calls on their own, each against HBM bandwidth. The "balance"
 object times the router's load-balancing calls on the step's own logits: one
 Quantile Balancing step (moe_qb_route, moe_qb_histogram with 1000 bins,
 moe_qb_update) and moe_aux_loss, each against HBM bandwidth.
