@@ -188,7 +188,7 @@ def _random_idx(T, E, k, seed, skew=False):
 
 @pytest.mark.parametrize("T,E,k,skew", [(64, 8, 2, False), (300, 37, 4, False), (1, 5, 3, False),
                                         (1000, 64, 8, True), (2049, 256, 4, False), (777, 896, 16, False),
-                                        (513, 1024, 2, True)])
+                                        (513, 1024, 2, True), (4000, 1024, 8, True)])
 def test_permute_vs_oracle(dev, moe, T, E, k, skew):
     d = 256
     idx = _random_idx(T, E, k, seed=T + E, skew=skew)
