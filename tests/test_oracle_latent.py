@@ -46,7 +46,7 @@ def _bf16_truncate(a):
 
 
 def _forward_norm_after_up(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, eps, w_proj_up,
-                           shared_gate, shared_up, shared_down, k, logits=None, bf16_operands=True):
+                           shared_gate, shared_up, shared_down, k, logits=None, bf16_operands=False):
     X = f64(x)
     E = f64(w_router).shape[0]
     L = orc.gate_logits(X, w_router, bias) if logits is None else f64(logits)
@@ -63,7 +63,7 @@ def _forward_norm_after_up(x, w_router, bias, w_proj_down, w_gate, w_up, w_down,
 
 
 def _forward_shared_inside_norm(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, eps, w_proj_up,
-                                shared_gate, shared_up, shared_down, k, logits=None, bf16_operands=True):
+                                shared_gate, shared_up, shared_down, k, logits=None, bf16_operands=False):
     res = _real_forward(x, w_router, bias, w_proj_down, w_gate, w_up, w_down, gain, eps, w_proj_up,
                         shared_gate, shared_up, shared_down, k, logits=logits, bf16_operands=bf16_operands)
     tot = res["up"]
@@ -98,3 +98,41 @@ def test_latent_pins_catch_planted_mistake(name, monkeypatch):
         except Exception as exc:
             caught.append((pin.__name__, type(exc).__name__))
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# ------------------------------------------------ the end-to-end rounding tolerance
+
+@pytest.mark.parametrize("case", [dict(), dict(T=77, d=128, l=256, E=12, k=3, h=256, n_shared=1, h_shared=256),
+                                  dict(T=1, E=5, k=2), dict(T=200, d=512, l=384, E=10, k=4, h=128),
+                                  dict(T=64, d=1024, l=1024, E=16, k=8, h=256, n_shared=2, h_shared=512)])
+def test_latent_error_model_covers_the_rounding_points(case):
+    """The tolerance the GPU test applies to the LatentMoE output, checked on the CPU
+    against the same three bf16 rounding points (z, H, r) applied inside the float64
+    layer: the rounded layer stays within 8 sigma of the unrounded one everywhere, and
+    the norm of the difference is what the first-order model predicts (within 30 %)."""
+    from synthetic import make_latent_inputs, scaled_latent
+    from tests import latent_bounds as lb
+    cfg = scaled_latent("latent_tiny", name="bounds", **case)
+    inp = make_latent_inputs(cfg)
+    exact = lat.latent_forward(inp.x, *inp.args(), k=cfg.k, bf16_operands=False)
+    rounded = lat.latent_forward(inp.x, *inp.args(), k=cfg.k, logits=exact["logits"], bf16_operands=True)
+    sigma = lb.latent_output_sigma(inp.x, inp.w_proj_down, inp.w_gate, inp.w_up, inp.w_down, inp.rms_gain,
+                                   inp.rms_eps, inp.w_proj_up, inp.shared_gate, inp.shared_up, inp.shared_down,
+                                   exact)
+    ratio, worst, _, _ = lb.check_latent_out(rounded["out"], exact["out"], sigma, factor=1.3)
+    assert ratio >= 0.7, f"the rounding model overstates the error {1 / ratio:.2f} times"
+    # a systematic mistake of a few bf16 ulps (a gain off by 3 %) fails the check
+    with pytest.raises(AssertionError):
+        lb.check_latent_out(exact["out"] + 0.03 * exact["up"], exact["out"], sigma)
+    # so does dropping one token's routed branch
+    broken = exact["out"].copy()
+    broken[0] -= exact["up"][0]
+    with pytest.raises(AssertionError):
+        lb.check_latent_out(broken, exact["out"], sigma)
+
+
+def test_ulp_bf16_values():
+    """bf16 spacing: 2^-7 in [1, 2), 2^-6 in [2, 4), 2^-8 in [0.5, 1); zero at 0."""
+    from tests import latent_bounds as lb
+    got = lb.ulp_bf16(np.array([1.0, 1.99, 2.0, -3.5, 0.75, 0.0]))
+    assert np.array_equal(got, [2.0 ** -7, 2.0 ** -7, 2.0 ** -6, 2.0 ** -6, 2.0 ** -8, 0.0])
