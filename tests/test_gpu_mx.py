@@ -2,7 +2,9 @@
 against the CPU oracle, through the C ABI.
 
   * codes and scales (weights, x rows, H rows): bit for bit (weights read back
-    from their matrix-core order as the header describes it). H's codes are
+    from their matrix-core order as the header describes it; every expert
+    matrix of every layer case, and whole expert matrices of the full prefill
+    layer). H's codes are
     compared with the oracle's quantisation of the device's own float32 H, so
     both sides decide on the same numbers;
   * H = silu(G) U from exact products accumulated in float32: with A_G, A_U
@@ -10,8 +12,8 @@ against the CPU oracle, through the C ABI.
     |dH| <= 1.1 gamma A_G |U| + (|G| + 0.3) gamma A_U + 1e-6 |H|;
   * Y rows: |dY| <= gamma_h * sum_k |h_k w_k| + 1e-30;
   * out against the oracle's combine of the device's Y rows: (k + 1) 2^-23 sum_j |w_j y_j|;
-  * the layer end to end against the oracle's own MX layer (device logits):
-    max rel <= 2e-2, mean abs <= 1e-3.
+  * the layer end to end against the oracle's own MX layer (device logits; x,
+    the weights and H quantised by the oracle): max rel <= 2e-2, mean abs <= 1e-3.
 """
 import numpy as np
 import pytest
@@ -142,8 +144,25 @@ def _check_y(y_dev, Hd, Wd):
     assert not bad.any(), f"Y: {bad.sum()} of {bad.size} off, worst excess {(err - bound).max():.3e}"
 
 
-def _oracle_mx_layer(inp, wts, logits, k):
-    """The oracle's MX layer on the device's logits (routing) and weight codes."""
+def _oracle_weights(w_bf16, e):
+    """The oracle's own MXFP4 quantisation of expert e's bf16 weight matrix, dequantised."""
+    codes, scales = mx.quantize(gu.f64(w_bf16[e]), mx.E2M1)
+    return mx.dequantize(codes, scales, mx.E2M1)
+
+
+def _check_weight_codes(wts, inp):
+    """The device's MXFP4 codes and scales of every expert matrix equal the oracle's, bit for bit."""
+    for pair, w, name in zip(wts, (inp.w_gate, inp.w_up, inp.w_down), ("gate", "up", "down")):
+        codes_ref, s_ref = mx.quantize(gu.f64(w), mx.E2M1)
+        codes = weight_codes(pair[0])
+        bad = np.argwhere(codes != codes_ref)
+        assert bad.size == 0, f"{name} E2M1 codes differ at {bad[:5].tolist()}"
+        assert np.array_equal(weight_scales(pair[1]), s_ref), f"{name} scales differ"
+
+
+def _oracle_mx_layer(inp, logits, k):
+    """The oracle's MX layer from the bf16 inputs: routing on the device's logits, x, the
+    weights and H quantised by the oracle itself."""
     E = inp.cfg.E
     idx, w, _ = orc.route(logits, k)
     off, row_of, row_src = orc.permute(idx, E)
@@ -154,10 +173,10 @@ def _oracle_mx_layer(inp, wts, logits, k):
         if hi == lo:
             continue
         rows = row_src[lo:hi]
-        H = orc.silu(mx.dequantize(xq[rows], xs[rows], mx.E4M3) @ _deq_w(wts[0], e).T) * \
-            (mx.dequantize(xq[rows], xs[rows], mx.E4M3) @ _deq_w(wts[1], e).T)
+        X = mx.dequantize(xq[rows], xs[rows], mx.E4M3)
+        H = orc.silu(X @ _oracle_weights(inp.w_gate, e).T) * (X @ _oracle_weights(inp.w_up, e).T)
         hq, hs = mx.quantize(H, mx.E4M3)
-        Y[lo:hi] = mx.dequantize(hq, hs, mx.E4M3) @ _deq_w(wts[2], e).T
+        Y[lo:hi] = mx.dequantize(hq, hs, mx.E4M3) @ _oracle_weights(inp.w_down, e).T
     return orc.combine(Y, row_of, w)
 
 
@@ -180,6 +199,7 @@ def test_mx_forward_matches_oracle(dev, moe, case):
     fwd = moe.MXForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
     out = fwd(di.x, di.w_router, di.router_bias, *wts)
     torch.cuda.synchronize()
+    _check_weight_codes(wts, inp)
     it = fwd.intermediate
     idx_ref, _ = gu.check_route(it("logits"), it("topk_idx"), it("topk_w"), cfg.k)
     off, row_of, row_src = gu.check_permutation(it("expert_offsets"), it("row_of"), it("row_src"), idx_ref, cfg.E)
@@ -204,7 +224,7 @@ def test_mx_forward_matches_oracle(dev, moe, case):
     bound = (cfg.k + 1) * 2.0 ** -23 * sum(np.abs(w[:, j:j + 1] * y[row_of[:, j]]) for j in range(cfg.k)) + 1e-30
     assert np.all(np.abs(gu.f64(out) - ref) <= bound)
     # end to end against the oracle's own MX layer
-    gu.check_layer(out, _oracle_mx_layer(inp, wts, gu.f64(it("logits")), cfg.k), "MX out")
+    gu.check_layer(out, _oracle_mx_layer(inp, gu.f64(it("logits")), cfg.k), "MX out")
     # and within the quantisation error of the bf16 layer
     plain = orc.forward(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down, cfg.k,
                         logits=gu.f64(it("logits")))["out"]
@@ -227,8 +247,9 @@ def test_mx_forward_deterministic(dev, moe):
 @pytest.mark.slow
 def test_mx_prefill_full_size_sampled(dev, moe):
     """The prefill layer (T = 8192, d = 7168, E = 256, top-4, h = 2048) with MXFP4 experts:
-    routing and permutation bit for bit, x's codes bit for bit, sampled weight rows' codes
-    bit for bit, and the H, Y and out rows of sampled tokens against the oracle."""
+    routing and permutation bit for bit, x's codes bit for bit, the whole gate, up and down
+    matrices of three experts and sampled weight rows of the routed ones bit for bit, and
+    the H, Y and out rows of sampled tokens against the oracle."""
     from synthetic import CONFIGS
     cfg = CONFIGS["prefill"]
     print("mx prefill: drawing inputs", flush=True)
@@ -238,6 +259,12 @@ def test_mx_prefill_full_size_sampled(dev, moe):
     out = fwd(inp.x, inp.w_router, None, *wts)
     torch.cuda.synchronize()
     print("mx prefill: forward done", flush=True)
+    for e in (0, 137, cfg.E - 1):  # whole expert matrices, every code and scale
+        for pair, w, name in zip(wts, (inp.w_gate, inp.w_up, inp.w_down), ("gate", "up", "down")):
+            codes_ref, s_ref = mx.quantize(gu.f64(w[e]), mx.E2M1)
+            assert np.array_equal(weight_codes(pair[0][e:e + 1])[0], codes_ref), f"{name} codes of expert {e}"
+            assert np.array_equal(weight_scales(pair[1][e:e + 1])[0], s_ref), f"{name} scales of expert {e}"
+    print("mx prefill: whole weight matrices of experts 0, 137, 255 match", flush=True)
     it = fwd.intermediate
     idx_ref, _ = gu.check_route(it("logits"), it("topk_idx"), it("topk_w"), cfg.k)
     off, row_of, row_src = gu.check_permutation(it("expert_offsets"), it("row_of"), it("row_src"), idx_ref, cfg.E)
