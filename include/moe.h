@@ -146,7 +146,13 @@ int moe_topk_softmax(const moe_shape_t* shape, const float* logits, int32_t* top
 
 /*
  * moe_permute -- group the T*k (token, slot) assignments by expert, stably, and
- * gather the token rows into expert order (the "grouped by expert" dispatch).
+ * gather the token rows into expert order: the dispatch of each token to the
+ * experts chosen for it ("Kimi K3: Open Frontier Intelligence", section
+ * "Operational Execution Flow", tokens dispatched to their active routed
+ * experts). The per-expert counts stay on the device (same page, section
+ * "Systems Optimization, Load Balancing, and Post-Training Alignment": token
+ * counts that change from batch to batch stall the device when the host has
+ * to wait for them).
  *
  *  x              [T, d]   bf16  (read; may be NULL when x_perm is NULL)
  *  topk_idx       [T, k]   int32 expert of each assignment, in [0, E) (read);
@@ -218,10 +224,14 @@ int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* ro
                 const float* topk_w, float* out, void* stream);
 
 /*
- * moe_forward -- the whole layer: moe_route, moe_permute (without x_perm),
- * moe_expert_ffn (reading x through row_src) and moe_combine in sequence on one
- * stream, intermediates in the workspace at the offsets moe_forward_ws_offset()
- * gives.
+ * moe_forward -- the whole routed layer: the gate, softmax and top-k of "Kimi
+ * K3: The Open Model That Just Cornered the AI Frontier", section
+ * "Mixture-of-Experts with Dynamic Load Balancing", then the probability-weighted
+ * sum of the selected SwiGLU experts' outputs of "Kimi K3: Open Frontier
+ * Intelligence", section "Operational Execution Flow". It runs moe_route,
+ * moe_permute (without x_perm), moe_expert_ffn (reading x through row_src) and
+ * moe_combine in sequence on one stream, intermediates in the workspace at the
+ * offsets moe_forward_ws_offset() gives.
  *
  *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL;
  *  w_gate, w_up [E, h, d] bf16; w_down [E, d, h] bf16 (all read)
