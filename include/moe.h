@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 8
+#define MOE_ABI_VERSION 9
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -170,6 +170,24 @@ int moe_topk_softmax(const moe_shape_t* shape, const float* logits, int32_t* top
 int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_idx,
                 int32_t* expert_offsets, int32_t* row_of, int32_t* row_src, uint16_t* x_perm,
                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, the same results bit
+ * for bit. Its scratch (the per-expert, per-chunk counts) lives in a fixed array
+ * of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call allocates nothing, on the device or the host. Every
+ * valid shape fits (E <= 1024 experts times at most 32 chunks of int32); a
+ * larger need would be rejected with MOE_ERR_UNSUPPORTED. Calls on one GPU share
+ * that GPU's array, so two calls that overlap in time on the same GPU (on
+ * different streams, or from different threads) race and may give wrong
+ * results; calls in order on one stream are safe. Nothing in the array needs to
+ * start at zero.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES 131072
+int moe_permute_noalloc(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_idx,
+                        int32_t* expert_offsets, int32_t* row_of, int32_t* row_src, uint16_t* x_perm, void* stream);
 
 /*
  * moe_expert_ffn -- every expert's SwiGLU FFN on its rows (grouped GEMM on bf16

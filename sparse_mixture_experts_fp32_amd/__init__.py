@@ -8,7 +8,7 @@ Using any op fails loudly if libmoe.so has not been built; the build module
 itself (`python -m sparse_mixture_experts_fp32_amd.build`) does not load it.
 """
 _OPS = ("LatentMoEForward", "MXForward", "MoEForward", "moe_mx_expert_ffn", "moe_mx_quantize_rows",
-        "moe_mx_quantize_weights", "moe_pack_weights", "moe_aux_loss", "moe_combine_rmsnorm", "moe_combine", "moe_expert_ffn", "moe_forward", "moe_permute",
+        "moe_mx_quantize_weights", "moe_pack_weights", "moe_aux_loss", "moe_combine_rmsnorm", "moe_combine", "moe_expert_ffn", "moe_forward", "moe_permute", "moe_permute_noalloc",
         "moe_qb_histogram", "moe_qb_route", "moe_qb_update", "moe_route", "moe_topk_softmax")
 
 __all__ = list(_OPS)

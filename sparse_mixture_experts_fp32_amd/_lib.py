@@ -30,7 +30,7 @@ MX_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src
 LAT_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "z", "h_act", "y_rows", "r",
              "shared_h", "shared_y"]
 FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 
 class MoeShape(ctypes.Structure):
@@ -66,6 +66,7 @@ def _load():
         "moe_route": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_topk_softmax": (ctypes.c_int, [S, P, P, P, P]),
         "moe_permute": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
+        "moe_permute_noalloc": (ctypes.c_int, [S, P, P, P, P, P, P, P]),
         "moe_expert_ffn": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_gate_up": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_expert_down": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_size_t, P]),

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -349,6 +350,69 @@ int moe_permute(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk
     if (st != MOE_OK) return st;
     hipError_t err = moe::launch_permute(x, topk_idx, shape->T, shape->d, shape->E, shape->k, expert_offsets,
                                          row_of, row_src, x_perm, static_cast<int32_t*>(ws), s);
+    return hip_status(err, "permute launch");
+}
+
+// ------------------------------------------------ moe_permute without a workspace
+// The permute's only scratch is the (expert, chunk) count matrix: E <= 1024 experts
+// times at most 32 chunks of int32, 128 KiB. moe_permute_noalloc keeps it in this
+// array, one copy per GPU for the life of the process. Host code never passes the
+// array's name to a kernel (on the host it only stands for the symbol): its device
+// address is looked up once per device with that device current and kept here.
+static __device__ __align__(256) int32_t scratch[MOE_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+int scratch_on_current_device(int32_t** out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return hip_status(err, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d this build tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return hip_status(err, "hipGetSymbolAddress(scratch)");
+        if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+}  // namespace
+
+int moe_permute_noalloc(const moe_shape_t* shape, const uint16_t* x, const int32_t* topk_idx,
+                        int32_t* expert_offsets, int32_t* row_of, int32_t* row_src, uint16_t* x_perm, void* stream) {
+    int st = check_shape(shape);
+    if (st != MOE_OK) return st;
+    MOE_CHECK_PTR(expert_offsets);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (shape->T == 0) {
+        hipError_t err = moe::launch_zero_i32(expert_offsets, shape->E + 1, s);
+        return hip_status(err, "expert_offsets clear");
+    }
+    MOE_CHECK_PTR(topk_idx);
+    MOE_CHECK_PTR(row_of);
+    MOE_CHECK_PTR(row_src);
+    if (x_perm != nullptr) {
+        MOE_CHECK_PTR(x);
+        if (!aligned16(x_perm)) return fail(MOE_ERR_INVALID_ARG, "x_perm is not 16-byte aligned");
+    }
+    const size_t need = permute_ws(shape);
+    if (need > MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_UNSUPPORTED, "permute scratch of %zu bytes exceeds the fixed %d bytes", need,
+                    MOE_NOALLOC_SCRATCH_BYTES);
+    int32_t* counts = nullptr;
+    st = scratch_on_current_device(&counts);
+    if (st != MOE_OK) return st;
+    // every count the scan and rank kernels read is written by this call's count kernel first,
+    // so what an earlier call left in the array does not matter
+    hipError_t err = moe::launch_permute(x, topk_idx, shape->T, shape->d, shape->E, shape->k, expert_offsets,
+                                         row_of, row_src, x_perm, counts, s);
     return hip_status(err, "permute launch");
 }
 

@@ -109,6 +109,32 @@ def moe_permute(x, topk_idx, E: int, gather: bool = True):
     return offsets, row_of, row_src, x_perm
 
 
+def moe_permute_noalloc(x, topk_idx, E: int, gather: bool = True, out=None):
+    """moe_permute through the entry point that allocates nothing: its scratch is a fixed
+    array inside the library. `out` may hold preallocated (expert_offsets, row_of, row_src,
+    x_perm) to write into; otherwise they are allocated here, by the caller's side."""
+    _need(x, "x", "bf16")
+    dev = x.device
+    T, d = x.shape
+    k = topk_idx.shape[1] if topk_idx.dim() == 2 else 1
+    _need(topk_idx, "topk_idx", "i32", (T, k), dev)
+    s = _lib.shape(T, d, E, k, 128)
+    if out is None:
+        out = (torch.empty(E + 1, dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.int32, device=dev),
+               torch.empty(T * k, dtype=torch.int32, device=dev),
+               torch.empty((T * k, d), dtype=torch.bfloat16, device=dev) if gather else None)
+    offsets, row_of, row_src, x_perm = out
+    _need(offsets, "expert_offsets", "i32", (E + 1,), dev)
+    _need(row_of, "row_of", "i32", (T, k), dev)
+    _need(row_src, "row_src", "i32", (T * k,), dev)
+    if x_perm is not None:
+        _need(x_perm, "x_perm", "bf16", (T * k, d), dev)
+    with torch.cuda.device(dev):
+        _lib.check(_lib.lib.moe_permute_noalloc(ctypes.byref(s), _ptr(x), _ptr(topk_idx), _ptr(offsets), _ptr(row_of),
+                                                _ptr(row_src), _ptr(x_perm), _stream(dev)))
+    return offsets, row_of, row_src, x_perm
+
+
 def _rows_operand(a, a_rows, T, k):
     """Validate the A operand of the grouped GEMM: x_perm [T*k, d], or x [T, d] with row_src [T*k]."""
     _need(a, "a", "bf16")

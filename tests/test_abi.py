@@ -56,7 +56,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 8
+    assert L.moe_abi_version() == lib.ABI_VERSION == 9
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -107,6 +107,26 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert L.moe_permute(ctypes.byref(s), None, a, a, a, a, a, a, 1 << 20, None) == 1
     assert L.moe_forward(ctypes.byref(s), a, a, None, a, a, a, None, a, 1 << 30, None) == 1
     assert L.moe_route(None, a, a, None, a, a, a, a, 1 << 30, None) == 1
+
+
+def test_noalloc_permute_checks_arguments(lib):
+    """moe_permute_noalloc validates like moe_permute (minus the workspace) before it looks
+    up its scratch array or launches anything."""
+    s = _shape(lib)
+    a = ctypes.c_void_p(4096)
+    mis = ctypes.c_void_p(4096 + 2)
+    L = lib.lib
+    assert L.moe_permute_noalloc(ctypes.byref(s), a, a, a, a, a, mis, None) == 1
+    assert b"x_perm" in L.moe_last_error()
+    assert L.moe_permute_noalloc(ctypes.byref(s), None, a, a, a, a, a, None) == 1
+    assert L.moe_permute_noalloc(ctypes.byref(s), a, None, a, a, a, None, None) == 1
+    assert L.moe_permute_noalloc(ctypes.byref(s), a, a, None, a, a, None, None) == 1
+    assert L.moe_permute_noalloc(ctypes.byref(s), a, a, a, a, None, None, None) == 1
+    assert L.moe_permute_noalloc(None, a, a, a, a, a, None, None) == 1
+    assert L.moe_permute_noalloc(ctypes.byref(_shape(lib, E=1025)), a, a, a, a, a, None, None) == 1
+    # the largest count matrix of any valid shape fits the fixed scratch
+    big = _shape(lib, T=4_000_000, E=1024, k=16)
+    assert L.moe_workspace_bytes(ctypes.byref(big), 0) == 1024 * 32 * 4 == 131072
 
 
 def test_workspace_checks(lib):
