@@ -10,7 +10,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIBRARY may name another build of the same library (the sanitizer build, libmoe_san.so)
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = 1

@@ -54,6 +54,27 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(declared_functions()) <= exported
 
 
+def test_probe_library_exports_its_header():
+    """libmoe_probe.so (the ceiling probes) exports every call include/moe_probe.h declares and
+    rejects bad arguments before launching anything."""
+    _ensure_built()
+    path = os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "libmoe_probe.so")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_[a-z_]+)\s*\(", text, flags=re.M)))
+    assert names == ["moe_probe_copy", "moe_probe_dma_read", "moe_probe_mfma", "moe_probe_read"]
+    L = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(L, n), n
+    a = ctypes.c_void_p(4096)
+    sz = ctypes.c_size_t
+    assert L.moe_probe_read(None, sz(16), a, None) == -1
+    assert L.moe_probe_read(a, sz(15), a, None) == -1
+    assert L.moe_probe_dma_read(a, sz(16), a, None) == -1          # not a whole 32 KiB stage
+    assert L.moe_probe_copy(a, ctypes.c_void_p(4096 + 16), sz(64), None) == -1  # overlapping
+    assert L.moe_probe_mfma(6, 10, a, None) == -1                  # waves not a multiple of 4
+    assert L.moe_probe_mfma(8, 40000, a, None) == -1               # beyond the exact range
+
+
 def test_status_strings(lib):
     L = lib.lib
     assert L.moe_abi_version() == lib.ABI_VERSION == 9
