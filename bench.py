@@ -63,9 +63,6 @@ def parse():
     ap.add_argument("--experts", choices=["bf16", "mxfp4"], default="bf16",
                     help="expert weight format: bf16, or MXFP4 weights with MXFP8 activations (weights quantised "
                          "once before the timed steps)")
-    ap.add_argument("--layout", choices=["packed", "rowmajor"], default="packed",
-                    help="bf16 expert weight layout: packed into 16 x 32 matrix-core tiles once before the timed "
-                         "steps (moe_pack_weights), or row-major [E, N, K]; both give the same output bit for bit")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure this chip's read, direct-to-LDS read, copy and bf16 matrix-core ceilings and "
                          "print them as one JSON line")
@@ -78,11 +75,11 @@ def parse():
 class Layer:
     """Preallocated buffers and C-ABI calls for one workload."""
 
-    def __init__(self, lib, inp, cfg, dev, weights=None, packed=False):
+    def __init__(self, lib, inp, cfg, dev, weights):
+        """weights: the packed (w_gate, w_up, w_down) of the workload."""
         import torch
         self.lib, self.inp, self.cfg, self.dev = lib, inp, cfg, dev
-        self.weights = weights if weights is not None else (inp.w_gate, inp.w_up, inp.w_down)
-        self.packed = packed
+        self.weights = weights
         T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
         n = T * k
         e = lambda *s, dt: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
@@ -115,14 +112,12 @@ class Layer:
         if ev is not None:
             ev[0].record(self.stream)
         wg, wu, wd = self.weights
-        gate_up = L.moe_expert_gate_up_packed if self.packed else L.moe_expert_gate_up
-        down = L.moe_expert_down_packed if self.packed else L.moe_expert_down
-        c(gate_up(sh, P(i.x), P(self.row_src), P(self.offsets), P(wg), P(wu), P(self.h_act),
-                  P(self.ws_ffn), self.ws_ffn.numel(), sp))
+        c(L.moe_expert_gate_up(sh, P(i.x), P(self.row_src), P(self.offsets), P(wg), P(wu), P(self.h_act),
+                               P(self.ws_ffn), self.ws_ffn.numel(), sp))
         if ev is not None:
             ev[1].record(self.stream)
-        c(down(sh, P(self.h_act), P(self.offsets), P(wd), P(self.y_rows), P(self.ws_ffn),
-               self.ws_ffn.numel(), sp))
+        c(L.moe_expert_down(sh, P(self.h_act), P(self.offsets), P(wd), P(self.y_rows), P(self.ws_ffn),
+                            self.ws_ffn.numel(), sp))
         if ev is not None:
             ev[2].record(self.stream)
         c(L.moe_combine(sh, P(self.y_rows), P(self.row_of), P(self.w), P(self.out), sp))
@@ -503,25 +498,22 @@ def latent_bench(args, dev, note):
     out = torch.empty((T, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    packed = args.layout == "packed"
-    wts = dict(w_proj_down=inp.w_proj_down, w_gate=inp.w_gate, w_up=inp.w_up, w_down=inp.w_down,
-               w_proj_up=inp.w_proj_up, shared_gate=inp.shared_gate, shared_up=inp.shared_up,
-               shared_down=inp.shared_down)
-    if packed:  # once, before timing; the row-major tensors stay for the check and the CPU baseline
-        from sparse_mixture_experts_fp32_amd import moe_pack_weights
-        for key, w in list(wts.items()):
-            if w is not None:
-                wts[key] = moe_pack_weights(w.unsqueeze(0)).squeeze(0) if w.dim() == 2 else moe_pack_weights(w)
-        torch.cuda.synchronize()
-        note("weights packed into matrix-core tiles")
+    # every bf16 weight converted once, before timing, to the library's packed layout (the
+    # row-major tensors stay for the CPU baseline)
+    from sparse_mixture_experts_fp32_amd import moe_pack_weights
+    wts = {}
+    for key in ("w_proj_down", "w_gate", "w_up", "w_down", "w_proj_up", "shared_gate", "shared_up", "shared_down"):
+        w = getattr(inp, key)
+        wts[key] = None if w is None else moe_pack_weights(w)
+    torch.cuda.synchronize()
+    note("weights packed into matrix-core tiles")
     args_c = [ctypes.byref(shape), P(inp.x), P(inp.w_router), None, P(wts["w_proj_down"]), P(wts["w_gate"]),
               P(wts["w_up"]), P(wts["w_down"]), P(inp.rms_gain), ctypes.c_float(inp.rms_eps), P(wts["w_proj_up"]),
               P(wts["shared_gate"]), P(wts["shared_up"]), P(wts["shared_down"]), P(out), P(ws), ws.numel(),
               ctypes.c_void_p(stream.cuda_stream)]
-    fn = lib.lib.moe_latent_forward_packed if packed else lib.lib.moe_latent_forward
 
     def step():
-        lib.check(fn(*args_c))
+        lib.check(lib.lib.moe_latent_forward(*args_c))
 
     for _ in range(args.warmup):
         step()
@@ -539,18 +531,6 @@ def latent_bench(args, dev, note):
     ms = (time.perf_counter() - t0) * 1e3 / K
     gpu_ms = start.elapsed_time(stop) / K
     note(f"{K} timed steps done")
-    if packed:  # the packed step equals moe_latent_forward on the row-major weights, bit for bit
-        ref = torch.empty_like(out)
-        ref_args = list(args_c)
-        for i, key in ((4, "w_proj_down"), (5, "w_gate"), (6, "w_up"), (7, "w_down"), (10, "w_proj_up"),
-                       (11, "shared_gate"), (12, "shared_up"), (13, "shared_down")):
-            ref_args[i] = P(getattr(inp, key))
-        ref_args[14] = P(ref)
-        lib.check(lib.lib.moe_latent_forward(*ref_args))
-        torch.cuda.synchronize()
-        assert torch.equal(ref, out), "packed LatentMoE step and moe_latent_forward disagree"
-        del ref
-        note("packed step equals moe_latent_forward (row-major weights) bit for bit")
     n = T * k
     flops = {"router": 2.0 * T * d * E, "down_projection": 2.0 * T * d * l, "routed_gate_up": 4.0 * n * l * h,
              "routed_down": 2.0 * n * l * h, "up_projection": 2.0 * T * l * d, "shared": 6.0 * S * T * d * hs}
@@ -562,10 +542,8 @@ def latent_bench(args, dev, note):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Stable LatentMoE, T={T} d={d} l={l} E={E} top-{k} h={h}, "
                                f"{S} shared experts of width {hs}, fp32 gate",
-                   "T": T, "d": d, "l": l, "E": E, "k": k, "h": h, "n_shared": S, "h_shared": hs, "seed": cfg.seed,
-                   "weight_layout": args.layout},
+                   "T": T, "d": d, "l": l, "E": E, "k": k, "h": h, "n_shared": S, "h_shared": hs, "seed": cfg.seed},
         "gpu_ms_per_step": gpu_ms,
-        "forward_calls": forward_calls,
         "flops": flops,
         "roofline": {"kernel": "whole LatentMoE step (every kernel of moe_latent_forward)", "bound": "mfma",
                      "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -751,13 +729,12 @@ def main():
             result["cpu_baseline"] = mx_cpu_baseline(inp, cfg, min(args.cpu_experts, 4))
         print(json.dumps(result), flush=True)
         return
-    packed = args.layout == "packed"
-    weights = None
-    if packed:  # once, before timing: the row-major tensors stay for the check and the CPU baseline
-        weights = tuple(moe_pack_weights(w) for w in (inp.w_gate, inp.w_up, inp.w_down))
-        torch.cuda.synchronize()
-        note("expert weights packed into matrix-core tiles")
-    layer = Layer(lib, inp, cfg, dev, weights, packed)
+    # once, before timing, the expert weights go into the library's packed layout (as a checkpoint
+    # would be converted on loading); the row-major tensors stay for the CPU baseline
+    weights = tuple(moe_pack_weights(w) for w in (inp.w_gate, inp.w_up, inp.w_down))
+    torch.cuda.synchronize()
+    note("expert weights packed into matrix-core tiles")
+    layer = Layer(lib, inp, cfg, dev, weights)
     note("buffers allocated")
 
     if args.copy_probe_mib > 0:
@@ -791,31 +768,23 @@ def main():
     gate_up_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
     down_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
 
-    # the step is moe_forward's kernel sequence on row-major weights: same output, bit for bit
+    # the step is moe_forward's kernel sequence: the one boundary call gives the same output, bit
+    # for bit, and is timed over a few calls of its own
     fwd = MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
-    ref_out = fwd(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down)
+    ref_out = fwd(inp.x, inp.w_router, inp.router_bias, *weights)
     torch.cuda.synchronize()
     assert torch.equal(ref_out, layer.out), "bench step and moe_forward disagree"
-    note("bench step equals moe_forward (row-major weights) bit for bit")
-    # the one-call boundary entry points themselves, timed over a few calls each
-    forward_calls = {}
+    note("bench step equals moe_forward bit for bit")
     reps = min(K, 10)
-    calls = [("moe_forward_rowmajor_ms", fwd, (inp.w_gate, inp.w_up, inp.w_down))]
-    if packed:
-        calls.append(("moe_forward_packed_ms", MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev, packed=True),
-                      weights))
-    for key, f, wts in calls:
-        f(inp.x, inp.w_router, inp.router_bias, *wts, out=ref_out)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(layer.stream)
-        for _ in range(reps):
-            f(inp.x, inp.w_router, inp.router_bias, *wts, out=ref_out)
-        b.record(layer.stream)
-        torch.cuda.synchronize()
-        assert torch.equal(ref_out, layer.out), f"{key}: output differs from the bench step"
-        forward_calls[key] = a.elapsed_time(b) / reps
-    forward_calls["reps"] = reps
-    del fwd, ref_out, calls
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(layer.stream)
+    for _ in range(reps):
+        fwd(inp.x, inp.w_router, inp.router_bias, *weights, out=ref_out)
+    b.record(layer.stream)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_out, layer.out), "moe_forward output differs from the bench step"
+    forward_calls = {"moe_forward_ms": a.elapsed_time(b) / reps, "reps": reps}
+    del fwd, ref_out
     note("moe_forward calls timed")
 
     T, d, E, k, h = cfg.T, cfg.d, cfg.E, cfg.k, cfg.h
@@ -832,10 +801,8 @@ def main():
     down_bytes = 2.0 * n * h + 2.0 * d * h * touched + 4.0 * n * d
     down_gbs = down_bytes / (down_ms * 1e-3) / 1e9
     ms = wall_ms
-    # the gate/up kernel: the LDS-ring kernel on packed weights, the register-streaming one on row-major
-    gu_name = ("ffn_ring_kernel<true, false>" if packed else
-               "grouped_ffn_kernel<moe::GemmCfg<1, 8, 2, 64, 12, true, 16>, true, false>")
-    gu_kernel = gu_name + (" (gate/up pass + SwiGLU, packed weights)" if packed else " (gate/up pass + SwiGLU)")
+    gu_name = "ffn_ring_kernel<true, false>"
+    gu_kernel = gu_name + " (gate/up pass + SwiGLU)"
     result = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -850,7 +817,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} top-{k} h={h}, SwiGLU experts, fp32 gate",
-                   "T": T, "d": d, "E": E, "k": k, "h": h, "seed": cfg.seed, "weight_layout": args.layout,
+                   "T": T, "d": d, "E": E, "k": k, "h": h, "seed": cfg.seed,
                    "experts_touched": touched, "max_rows_per_expert": int(counts.max())},
         "gpu_ms_per_step": gpu_ms,
         "forward_calls": forward_calls,

@@ -18,11 +18,16 @@
  *    moe_aux_loss is the first page's auxiliary balance loss.
  *
  * Conventions shared by every call
- *  - All tensors are dense, row-major (C order), on the device, 16-byte
- *    aligned. bfloat16 values are passed as uint16_t bit patterns.
- *  - Weights are stored output-major, input-contiguous (the layout of a linear
+ *  - All tensors are dense, on the device, 16-byte aligned; activations and
+ *    every other buffer row-major (C order), bf16 weight matrices in the packed
+ *    layout below. bfloat16 values are passed as uint16_t bit patterns.
+ *  - Weights are output-major, input-contiguous matrices (the layout of a linear
  *    layer's weight): w_router [E, d] float32; w_gate, w_up [E, h, d] bf16;
  *    w_down [E, d, h] bf16. So logits = x w_router^T, gate = x w_gate[e]^T.
+ *    The bf16 matrices of the expert and projection passes are held in the
+ *    library's packed layout (matrix-core fragment order, see moe_pack_weights):
+ *    a row-major checkpoint is converted once with moe_pack_weights, as a
+ *    quantised one would be quantised once. The router weight stays row-major.
  *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *    enqueues kernels on it and returns; nothing is synchronised, nothing is
  *    copied to the host, nothing is allocated or freed by the library. The
@@ -46,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 9
+#define MOE_ABI_VERSION 10
 
 typedef struct moe_shape {
     int64_t T; /* tokens in the batch */
@@ -201,8 +206,8 @@ int moe_permute_noalloc(const moe_shape_t* shape, const uint16_t* x, const int32
  *                 gather done inside the GEMM; ids are clamped to [0, T))
  *  expert_offsets [E + 1]    int32 as written by moe_permute (read; only the
  *                            device copy is used, the host never sees it)
- *  w_gate, w_up   [E, h, d]  bf16 (read)
- *  w_down         [E, d, h]  bf16 (read)
+ *  w_gate, w_up   [E, h, d]  bf16, packed (moe_pack_weights with E groups, N = h, K = d) (read)
+ *  w_down         [E, d, h]  bf16, packed (E groups, N = d, K = h) (read)
  *  h_act          [T * k, h] bf16 out: silu(x w_gate[e]^T) * (x w_up[e]^T), rounded once
  *  y_rows         [T * k, d] float32 out: h_act w_down[e]^T (float32 accumulation)
  *  ws, ws_bytes   workspace of at least moe_workspace_bytes(shape, MOE_CALL_EXPERT_FFN)
@@ -252,7 +257,7 @@ int moe_combine(const moe_shape_t* shape, const float* y_rows, const int32_t* ro
  * offsets moe_forward_ws_offset() gives.
  *
  *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL;
- *  w_gate, w_up [E, h, d] bf16; w_down [E, d, h] bf16 (all read)
+ *  w_gate, w_up [E, h, d] bf16 packed; w_down [E, d, h] bf16 packed (all read)
  *  out [T, d] float32 (written)
  *  ws, ws_bytes  workspace of at least moe_workspace_bytes(shape, MOE_CALL_FORWARD)
  */
@@ -325,14 +330,15 @@ int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float
 
 /*
  * ------------------------------------------------------------ packed weights
- * Expert weights stored in matrix-core fragment order: a weight matrix [N, K] is
+ * The library's weight format for bf16 matrices (the expert, shared-expert and
+ * projection weights): matrix-core fragment order. A weight matrix [N, K] is
  * cut into tiles of 16 rows x 32 columns, 512 contiguous elements each, in
  * (row block, column block) order; inside a tile, element (r, c) sits at
  * (r + 16 * (c / 8)) * 8 + c % 8, which is the order in which the 64 lanes of a
  * wavefront hold one 16 x 32 MFMA operand (lane l: row l % 16, columns
  * 8 * (l / 16) .. + 7). One kilobyte of HBM then is one operand, loaded in one
- * contiguous run straight into LDS. The values are the same; the *_packed calls
- * give bitwise the results of their row-major counterparts.
+ * contiguous run straight into LDS. The values are those of the row-major
+ * matrix, only their order differs.
  *
  * moe_pack_weights: w [groups, N, K] bf16 row-major (read) -> w_packed, the same
  *  number of elements in packed order (written; must not overlap w). N a
@@ -340,15 +346,6 @@ int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float
  */
 int moe_pack_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint16_t* w_packed,
                      void* stream);
-/* moe_expert_gate_up, moe_expert_down and moe_forward with packed expert weights. */
-int moe_expert_gate_up_packed(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
-                              const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
-                              uint16_t* h_act, void* ws, size_t ws_bytes, void* stream);
-int moe_expert_down_packed(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
-                           const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream);
-int moe_forward_packed(const moe_shape_t* shape, const uint16_t* x, const float* w_router,
-                       const float* router_bias, const uint16_t* w_gate, const uint16_t* w_up,
-                       const uint16_t* w_down, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ---------------------------------------------------------------- LatentMoE
@@ -360,8 +357,9 @@ int moe_forward_packed(const moe_shape_t* shape, const uint16_t* x, const float*
  *   out = W_up_proj RMSNorm(u) + sum_s SharedExpert_s(x),
  *   u = sum_{j<k} w[t, j] E_{idx[t, j]}(z),  z = W_down_proj x,
  *   RMSNorm(u) = g * u / sqrt(mean u^2 + eps).
- * Every expert is SwiGLU. z and RMSNorm(u) are rounded to bf16 (they are
- * matrix-core operands); u, the expert outputs and out are float32.
+ * Every expert is SwiGLU. z, every expert's SwiGLU activation and RMSNorm(u)
+ * are rounded to bf16 (they are matrix-core operands); u, the expert outputs
+ * and out are float32.
  */
 typedef struct moe_latent_shape {
     int64_t T;        /* tokens */
@@ -398,10 +396,11 @@ int moe_latent_ws_offset(const moe_latent_shape_t* shape, int slot, size_t* offs
 /*
  * moe_latent_forward -- the whole LatentMoE layer on one stream.
  *  x [T, d] bf16; w_router [E, d] f32; router_bias [E] f32 or NULL
- *  w_proj_down [l, d] bf16; w_gate, w_up [E, h, l] bf16; w_down [E, l, h] bf16
- *  rms_gain [l] f32; rms_eps >= 0 (finite); w_proj_up [d, l] bf16
- *  shared_gate, shared_up [n_shared, h_shared, d] bf16; shared_down [n_shared, d, h_shared] bf16
- *    (all three may be NULL when n_shared = 0)
+ *  every bf16 matrix packed (moe_pack_weights; the projections as one group each):
+ *  w_proj_down [l, d]; w_gate, w_up [E, h, l]; w_down [E, l, h]; w_proj_up [d, l];
+ *  shared_gate, shared_up [n_shared, h_shared, d]; shared_down [n_shared, d, h_shared]
+ *    (the shared three may be NULL when n_shared = 0)
+ *  rms_gain [l] f32; rms_eps >= 0 (finite)
  *  out [T, d] float32 (written)
  *  ws, ws_bytes  workspace of at least moe_latent_workspace_bytes(shape)
  * Sums: u in slot order; out = ((W_up_proj r) + shared_0) + shared_1 ...
@@ -411,14 +410,6 @@ int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const
                        const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
                        const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
                        const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream);
-/* moe_latent_forward with every bf16 weight in packed order (moe_pack_weights: w_proj_down as 1 group
- * [l, d], w_proj_up as 1 group [d, l], the routed and shared expert tensors as E and n_shared groups);
- * same workspace, bitwise the same out. */
-int moe_latent_forward_packed(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
-                              const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
-                              const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
-                              const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
-                              const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine_rmsnorm -- the routed sum followed by the RMSNorm, in one pass

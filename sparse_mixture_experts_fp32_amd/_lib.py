@@ -31,7 +31,7 @@ MX_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src
 LAT_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "z", "h_act", "y_rows", "r",
              "shared_h", "shared_y"]
 FWD_SLOTS = ["logits", "topk_idx", "topk_w", "expert_offsets", "row_of", "row_src", "h_act", "y_rows"]
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 
 class MoeShape(ctypes.Structure):
@@ -75,9 +75,6 @@ def _load():
         "moe_forward": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_aux_loss": (ctypes.c_int, [S, P, P, P, P, ctypes.c_size_t, P]),
         "moe_pack_weights": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P]),
-        "moe_expert_gate_up_packed": (ctypes.c_int, [S, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
-        "moe_expert_down_packed": (ctypes.c_int, [S, P, P, P, P, P, ctypes.c_size_t, P]),
-        "moe_forward_packed": (ctypes.c_int, [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]),
         "moe_qb_route": (ctypes.c_int, [S, P, P, P, P, P, P]),
         "moe_qb_histogram": (ctypes.c_int, [S, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32, P, P]),
         "moe_qb_update": (ctypes.c_int, [S, P, ctypes.c_float, ctypes.c_float, ctypes.c_int32, P, P, P]),
@@ -85,8 +82,6 @@ def _load():
         "moe_latent_ws_offset": (ctypes.c_int, [LS, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
         "moe_latent_forward": (ctypes.c_int, [LS, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
                                               ctypes.c_size_t, P]),
-        "moe_latent_forward_packed": (ctypes.c_int, [LS, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P,
-                                                     ctypes.c_size_t, P]),
         "moe_combine_rmsnorm": (ctypes.c_int, [S, P, P, P, P, ctypes.c_float, P, P, P]),
         "moe_mx_quantize_weights": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
         "moe_mx_quantize_rows": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, P, ctypes.c_int32, P, P, P]),

@@ -31,7 +31,7 @@ LIB_PROBE = os.path.join(PKG, "libmoe_probe.so")
 LIB_SAN = os.path.join(PKG, "libmoe_san.so")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "ffn_ring.hip", "combine.hip", "balance.hip", "latent.hip", "mx.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "tiles.hip", "ffn_ring.hip", "combine.hip", "balance.hip", "latent.hip", "mx.hip", "moe_api.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 # host-side sanitizers only (each -fsanitize= right after -Xarch_host: device code is built as usual)
 SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",

@@ -1,16 +1,25 @@
-// Grouped GEMM over experts with an LDS ring fed by direct-to-LDS loads: the
-// expert SwiGLU FFN of "Kimi K3: Open Frontier Intelligence", section
-// "Operational Execution Flow" (SwiGLU-form experts applied to the rows routed
-// to them), for packed expert weights.
+// Grouped GEMM over experts on bf16 MFMA with float32 accumulation, an LDS ring
+// fed by direct-to-LDS loads: the expert SwiGLU FFN of "Kimi K3: Open Frontier
+// Intelligence", section "Operational Execution Flow" (SwiGLU-form experts
+// applied to the rows routed to them). Expert weights are in the packed layout
+// below (moe_pack_weights converts a row-major [N, K] matrix once).
 //
 //   gate/up pass: H[r, n] = silu(sum_i A[r, i] Wg[e, n, i]) * (sum_i A[r, i] Wu[e, n, i])
 //   down pass:    Y[r, n] = sum_i H[r, i] Wd[e, n, i]
+// for every row r of expert e. H is rounded once to bf16 (the down pass's MFMA
+// operand); Y stays float32. Each output is a sum over K in steps of 32, one
+// 16x16x32 MFMA per step and output block, in ascending K.
 //
-// Same work units and schedule as grouped_ffn_kernel (m-tiles of up to 192 rows
-// of one expert from build_tiles_kernel, XCD-ordered), same products in the same
-// order (K in steps of 32, one MFMA per step and output block), so the results
-// are bitwise those of the register-streaming kernel; what differs is where the
-// operands wait:
+// Work unit: one m-tile of up to 192 rows of one expert (tiles.hip) x one
+// n-tile of 512 weight rows. Scheduling for the 8 XCDs (each with its own L2):
+// workgroup ids are dealt to the XCDs round-robin, so XCD x runs ids x, x + 8,
+// ... in order. The m-tile list is cut into 8 contiguous chunks, one per XCD,
+// and inside a chunk the work is ordered expert by expert, n-tile by n-tile,
+// with the expert's m-tiles innermost: the m-tiles that share one weight n-tile
+// run side by side on one XCD and fetch those weights from HBM once, and all
+// n-tiles of an expert follow each other, so its A rows stay in that L2.
+//
+// Where the operands wait:
 //
 //  * Every operand byte goes from HBM/L2 straight into LDS with
 //    global_load_lds_dwordx4 (64 lanes x 16 B = 1 KiB per instruction, no
@@ -189,7 +198,7 @@ void ffn_ring_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__
     constexpr int kColsWG = kColsW * kRWaves;
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kRStages * kRStage];
 
-    // ---- work item: (m-tile, n-tile) from the XCD-ordered schedule (as grouped_ffn_kernel)
+    // ---- work item: (m-tile, n-tile) from the XCD-ordered schedule
     const int n_mt = tile_start[E];
     const int xcd = blockIdx.x % kXcdsR;
     const int j = blockIdx.x / kXcdsR;
@@ -259,21 +268,21 @@ static hipError_t launch_ring(const uint16_t* A, const int32_t* A_rows, int64_t 
     return hipGetLastError();
 }
 
-hipError_t launch_gate_up_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
-                               const int32_t* tile_start, int64_t n_rows, int d, int E, int h,
-                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, hipStream_t stream) {
+hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                          const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,
+                          const uint16_t* w_up, uint16_t* h_act, hipStream_t stream) {
     return launch_ring<true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w_gate, w_up, h, d, h_act, stream);
 }
 
-hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
-                            int d, int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream) {
+hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
+                       int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream) {
     return launch_ring<false>(h_act, nullptr, n_rows, tiles, tile_start, n_rows, E, w_down, nullptr, d, h, y_rows,
                               stream);
 }
 
-hipError_t launch_dense_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
-                             const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
-                             bool bf16_out, hipStream_t stream) {
+hipError_t launch_dense(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
+                        bool bf16_out, hipStream_t stream) {
     if (bf16_out)
         return launch_ring<false, true>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c, stream);
     return launch_ring<false, false>(a, a_rows, a_nrows, tiles, tile_start, n_rows, E, w, nullptr, N, K, c, stream);

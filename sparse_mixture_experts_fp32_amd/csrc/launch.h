@@ -26,24 +26,20 @@ hipError_t launch_build_tiles(const int32_t* expert_offsets, int64_t n_rows, int
 // the same with m-tiles of up to bm rows (bm >= 128, a multiple of 16)
 hipError_t launch_build_tiles_rows(const int32_t* expert_offsets, int64_t n_rows, int E, int bm, int4* tiles,
                                    int32_t* tile_start, hipStream_t stream);
-// a_rows == nullptr: GEMM row r is a[r] (a = x_perm); else it is a[a_rows[r]] (a = x with a_nrows rows).
+// The expert GEMM passes on the LDS-ring kernel (ffn_ring.hip); expert weights in the packed
+// layout of moe_pack_weights. a_rows == nullptr: GEMM row r is a[r] (a = x_perm); else it is
+// a[a_rows[r]] (a = x with a_nrows rows).
 hipError_t launch_gate_up(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
                           const int32_t* tile_start, int64_t n_rows, int d, int E, int h, const uint16_t* w_gate,
-                          const uint16_t* w_up, uint16_t* h_act, hipStream_t stream, bool packed = false);
+                          const uint16_t* w_up, uint16_t* h_act, hipStream_t stream);
 hipError_t launch_down(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows, int d,
-                       int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream, bool packed = false);
+                       int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream);
+// plain products c = a w^T per group (bf16 or float32 out)
+hipError_t launch_dense(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
+                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
+                        bool bf16_out, hipStream_t stream);
 // row-major bf16 [rows, K] (rows % 16 == 0, K % 32 == 0) -> packed 16 x 32 fragment-order tiles
 hipError_t launch_pack_weights(const uint16_t* w, int64_t rows, int K, uint16_t* out, hipStream_t stream);
-// the expert passes on the LDS-ring kernel (packed weights; the same tile list as launch_gate_up/launch_down)
-hipError_t launch_gate_up_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
-                               const int32_t* tile_start, int64_t n_rows, int d, int E, int h,
-                               const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act, hipStream_t stream);
-hipError_t launch_down_ring(const uint16_t* h_act, const int4* tiles, const int32_t* tile_start, int64_t n_rows,
-                            int d, int E, int h, const uint16_t* w_down, float* y_rows, hipStream_t stream);
-// plain products c = a w^T per group on packed weights (bf16 or float32 out), as launch_dense
-hipError_t launch_dense_ring(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
-                             const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
-                             bool bf16_out, hipStream_t stream);
 
 hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T,
                           int d, int k, int64_t n_rows, float* out, hipStream_t stream);
@@ -58,10 +54,6 @@ hipError_t launch_qb_update(const int32_t* hist, int E, int k, int n_bins, float
 size_t aux_ws_bytes(int64_t T, int E);
 hipError_t launch_aux_loss(const float* logits, int64_t T, int E, float* prob_mean, float* aux_loss, void* ws,
                            hipStream_t stream);
-
-hipError_t launch_dense(const uint16_t* a, const int32_t* a_rows, int64_t a_nrows, const int4* tiles,
-                        const int32_t* tile_start, int64_t n_rows, int E, const uint16_t* w, int N, int K, void* c,
-                        bool bf16_out, hipStream_t stream);
 
 int combine_rmsnorm_max_width();
 hipError_t launch_combine_rmsnorm(const float* y_rows, const int32_t* row_of, const float* topk_w, int64_t T, int l,

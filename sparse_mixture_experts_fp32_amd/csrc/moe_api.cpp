@@ -444,9 +444,9 @@ int moe_expert_ffn(const moe_shape_t* shape, const uint16_t* a, const int32_t* a
     return hip_status(err, "down launch");
 }
 
-static int expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
-                          const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
-                          uint16_t* h_act, void* ws, size_t ws_bytes, void* stream, bool packed) {
+int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
+                       const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
+                       void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -464,24 +464,12 @@ static int expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int
     hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
     err = moe::launch_gate_up(a, a_rows, shape->T, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h,
-                              w_gate, w_up, h_act, s, packed);
+                              w_gate, w_up, h_act, s);
     return hip_status(err, "gate_up launch");
 }
 
-int moe_expert_gate_up(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
-                       const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up, uint16_t* h_act,
-                       void* ws, size_t ws_bytes, void* stream) {
-    return expert_gate_up(shape, a, a_rows, expert_offsets, w_gate, w_up, h_act, ws, ws_bytes, stream, false);
-}
-
-int moe_expert_gate_up_packed(const moe_shape_t* shape, const uint16_t* a, const int32_t* a_rows,
-                              const int32_t* expert_offsets, const uint16_t* w_gate, const uint16_t* w_up,
-                              uint16_t* h_act, void* ws, size_t ws_bytes, void* stream) {
-    return expert_gate_up(shape, a, a_rows, expert_offsets, w_gate, w_up, h_act, ws, ws_bytes, stream, true);
-}
-
-static int expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
-                       const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream, bool packed) {
+int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
+                    const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -496,19 +484,8 @@ static int expert_down(const moe_shape_t* shape, const uint16_t* h_act, const in
     const FfnWs fw = ffn_carve(shape, ws);
     hipError_t err = moe::launch_build_tiles(expert_offsets, n, shape->E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s,
-                           packed);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, shape->d, shape->E, shape->h, w_down, y_rows, s);
     return hip_status(err, "down launch");
-}
-
-int moe_expert_down(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
-                    const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
-    return expert_down(shape, h_act, expert_offsets, w_down, y_rows, ws, ws_bytes, stream, false);
-}
-
-int moe_expert_down_packed(const moe_shape_t* shape, const uint16_t* h_act, const int32_t* expert_offsets,
-                           const uint16_t* w_down, float* y_rows, void* ws, size_t ws_bytes, void* stream) {
-    return expert_down(shape, h_act, expert_offsets, w_down, y_rows, ws, ws_bytes, stream, true);
 }
 
 int moe_pack_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint16_t* w_packed, void* stream) {
@@ -600,9 +577,9 @@ int moe_qb_update(const moe_shape_t* shape, const int32_t* hist, float lo, float
     return hip_status(err, "qb_update launch");
 }
 
-static int forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
-                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
-                   size_t ws_bytes, void* stream, bool packed) {
+int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
+                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
+                size_t ws_bytes, void* stream) {
     int st = check_shape(shape);
     if (st != MOE_OK) return st;
     if (shape->T == 0) return ok();
@@ -644,25 +621,14 @@ static int forward(const moe_shape_t* shape, const uint16_t* x, const float* w_r
     if (err != hipSuccess) return hip_status(err, "permute launch");
     err = moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s);
     if (err != hipSuccess) return hip_status(err, "build_tiles launch");
-    err = moe::launch_gate_up(x, row_src, T, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s, packed);
+    err = moe::launch_gate_up(x, row_src, T, fw.tiles, fw.tile_start, n, d, E, h, w_gate, w_up, h_act, s);
     if (err != hipSuccess) return hip_status(err, "gate_up launch");
-    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, d, E, h, w_down, y_rows, s, packed);
+    err = moe::launch_down(h_act, fw.tiles, fw.tile_start, n, d, E, h, w_down, y_rows, s);
     if (err != hipSuccess) return hip_status(err, "down launch");
     err = moe::launch_combine(y_rows, row_of, w, T, d, k, n, out, s);
     return hip_status(err, "combine launch");
 }
 
-int moe_forward(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
-                const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
-                size_t ws_bytes, void* stream) {
-    return forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, out, ws, ws_bytes, stream, false);
-}
-
-int moe_forward_packed(const moe_shape_t* shape, const uint16_t* x, const float* w_router, const float* router_bias,
-                       const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down, float* out, void* ws,
-                       size_t ws_bytes, void* stream) {
-    return forward(shape, x, w_router, router_bias, w_gate, w_up, w_down, out, ws, ws_bytes, stream, true);
-}
 
 size_t moe_latent_workspace_bytes(const moe_latent_shape_t* shape) {
     if (check_latent_shape(shape) != MOE_OK) return 0;
@@ -703,12 +669,11 @@ int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int
     return hip_status(err, "combine_rmsnorm launch");
 }
 
-static int latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
-                          const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
-                          const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
-                          const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
-                          const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream,
-                          bool packed) {
+int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
+                       const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
+                       const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
+                       const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
+                       const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
     int st = check_latent_shape(shape);
     if (st != MOE_OK) return st;
     if (!std::isfinite(rms_eps) || rms_eps < 0.f) return fail(MOE_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
@@ -775,25 +740,23 @@ static int latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, co
             "permute launch");
     // z = x W_down_proj^T (bf16)
     MOE_TRY(moe::launch_build_tiles(dense_off, T, 1, dw.tiles, dw.tile_start, s), "build_tiles launch");
-    MOE_TRY(packed ? moe::launch_dense_ring(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s)
-                   : moe::launch_dense(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s),
+    MOE_TRY(moe::launch_dense(x, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_down, l, d, z, true, s),
             "down projection launch");
     // routed experts on z (rows gathered through row_src), then u and RMSNorm(u)
     MOE_TRY(moe::launch_build_tiles(offsets, n, E, fw.tiles, fw.tile_start, s), "build_tiles launch");
-    MOE_TRY(moe::launch_gate_up(z, row_src, T, fw.tiles, fw.tile_start, n, l, E, h, w_gate, w_up, h_act, s, packed),
+    MOE_TRY(moe::launch_gate_up(z, row_src, T, fw.tiles, fw.tile_start, n, l, E, h, w_gate, w_up, h_act, s),
             "gate_up launch");
-    MOE_TRY(moe::launch_down(h_act, fw.tiles, fw.tile_start, n, l, E, h, w_down, y_rows, s, packed), "down launch");
+    MOE_TRY(moe::launch_down(h_act, fw.tiles, fw.tile_start, n, l, E, h, w_down, y_rows, s), "down launch");
     MOE_TRY(moe::launch_combine_rmsnorm(y_rows, row_of, w, T, l, k, n, rms_gain, rms_eps, nullptr, r, s),
             "combine_rmsnorm launch");
     // out = RMSNorm(u) W_up_proj^T (float32) ...
-    MOE_TRY(packed ? moe::launch_dense_ring(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s)
-                   : moe::launch_dense(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s),
+    MOE_TRY(moe::launch_dense(r, nullptr, T, dw.tiles, dw.tile_start, T, 1, w_proj_up, d, l, out, false, s),
             "up projection launch");
     if (S > 0) {  // ... + the shared experts on x
         MOE_TRY(moe::launch_build_tiles(shared_off, T * S, S, sw.tiles, sw.tile_start, s), "build_tiles launch");
         MOE_TRY(moe::launch_gate_up(x, shared_rows, T, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_gate,
-                                    shared_up, sh_h, s, packed), "shared gate_up launch");
-        MOE_TRY(moe::launch_down(sh_h, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_down, sh_y, s, packed),
+                                    shared_up, sh_h, s), "shared gate_up launch");
+        MOE_TRY(moe::launch_down(sh_h, sw.tiles, sw.tile_start, T * S, d, S, hs, shared_down, sh_y, s),
                 "shared down launch");
         MOE_TRY(moe::launch_add_shared(out, sh_y, T, d, S, s), "add_shared launch");
     }
@@ -801,23 +764,6 @@ static int latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, co
     return ok();
 }
 
-int moe_latent_forward(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
-                       const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
-                       const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
-                       const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
-                       const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
-    return latent_forward(shape, x, w_router, router_bias, w_proj_down, w_gate, w_up, w_down, rms_gain, rms_eps,
-                          w_proj_up, shared_gate, shared_up, shared_down, out, ws, ws_bytes, stream, false);
-}
-
-int moe_latent_forward_packed(const moe_latent_shape_t* shape, const uint16_t* x, const float* w_router,
-                              const float* router_bias, const uint16_t* w_proj_down, const uint16_t* w_gate,
-                              const uint16_t* w_up, const uint16_t* w_down, const float* rms_gain, float rms_eps,
-                              const uint16_t* w_proj_up, const uint16_t* shared_gate, const uint16_t* shared_up,
-                              const uint16_t* shared_down, float* out, void* ws, size_t ws_bytes, void* stream) {
-    return latent_forward(shape, x, w_router, router_bias, w_proj_down, w_gate, w_up, w_down, rms_gain, rms_eps,
-                          w_proj_up, shared_gate, shared_up, shared_down, out, ws, ws_bytes, stream, true);
-}
 
 int moe_mx_quantize_weights(int64_t groups, int32_t N, int32_t K, const uint16_t* w, uint8_t* q, uint8_t* scales,
                             void* stream) {

@@ -36,6 +36,14 @@ def _need(t, name, dtype, shape=None, device=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _need_packed(t, name, shape, device):
+    """A bf16 weight tensor in the library's packed layout (made by moe_pack_weights)."""
+    _need(t, name, "bf16", shape, device)
+    if not getattr(t, "moe_packed", False):
+        raise TypeError(f"{name} must be in the packed weight layout: convert the row-major tensor once with "
+                        f"moe_pack_weights")
+
+
 def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
@@ -153,14 +161,15 @@ def _rows_operand(a, a_rows, T, k):
 def moe_expert_ffn(a, expert_offsets, w_gate, w_up, w_down, T: int, k: int, a_rows=None):
     """h_act [T*k, h] bf16 and y_rows [T*k, d] f32 for rows grouped by expert.
 
-    The rows are a = x_perm [T*k, d] (a_rows None), or a = x [T, d] read through a_rows = row_src [T*k]."""
+    The rows are a = x_perm [T*k, d] (a_rows None), or a = x [T, d] read through a_rows = row_src [T*k].
+    The expert weights are packed (moe_pack_weights)."""
     dev, d = _rows_operand(a, a_rows, T, k)
     n = T * k
     E, h, _ = w_gate.shape
     _need(expert_offsets, "expert_offsets", "i32", (E + 1,), dev)
-    _need(w_gate, "w_gate", "bf16", (E, h, d), dev)
-    _need(w_up, "w_up", "bf16", (E, h, d), dev)
-    _need(w_down, "w_down", "bf16", (E, d, h), dev)
+    _need_packed(w_gate, "w_gate", (E, h, d), dev)
+    _need_packed(w_up, "w_up", (E, h, d), dev)
+    _need_packed(w_down, "w_down", (E, d, h), dev)
     s = _lib.shape(T, d, E, k, h)
     h_act = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
     y_rows = torch.empty((n, d), dtype=torch.float32, device=dev)
@@ -191,24 +200,24 @@ def moe_combine(y_rows, row_of, topk_w):
 
 
 def moe_pack_weights(w):
-    """Expert weights w [G, N, K] bf16 in matrix-core order (16-row x 32-column tiles of
-    512 contiguous elements, each one MFMA operand in lane order): the same values, a new
-    tensor of the same shape whose memory is in packed order (for
-    MoEForward(..., packed=True) and the *_packed calls)."""
+    """Row-major bf16 weights w ([G, N, K] expert tensors, or one [N, K] matrix) in the library's
+    packed layout (16-row x 32-column tiles of 512 contiguous elements, each one MFMA operand in
+    lane order): a new tensor of the same shape and values whose memory is in packed order, the
+    form every layer call takes. A one-time conversion, like loading a checkpoint."""
     _need(w, "w", "bf16")
     dev = w.device
-    G, N, K = w.shape
+    G, N, K = (1, *w.shape) if w.dim() == 2 else w.shape
     out = torch.empty_like(w)
     with torch.cuda.device(dev):
         _lib.check(_lib.lib.moe_pack_weights(G, N, K, _ptr(w), _ptr(out), _stream(dev)))
+    out.moe_packed = True
     return out
 
 
 class MoEForward:
-    """moe_forward (moe_forward_packed when packed) with a reusable workspace."""
+    """moe_forward with a reusable workspace; expert weights packed (moe_pack_weights)."""
 
-    def __init__(self, T: int, d: int, E: int, k: int, h: int, device, packed: bool = False):
-        self.packed = packed
+    def __init__(self, T: int, d: int, E: int, k: int, h: int, device):
         self.shape = _lib.shape(T, d, E, k, h)
         self.T, self.d, self.E, self.k, self.h = T, d, E, k, h
         self.device = torch.device(device)
@@ -220,15 +229,14 @@ class MoEForward:
         _need(w_router, "w_router", "f32", (E, d), dev)
         if router_bias is not None:
             _need(router_bias, "router_bias", "f32", (E,), dev)
-        _need(w_gate, "w_gate", "bf16", (E, h, d), dev)
-        _need(w_up, "w_up", "bf16", (E, h, d), dev)
-        _need(w_down, "w_down", "bf16", (E, d, h), dev)
+        _need_packed(w_gate, "w_gate", (E, h, d), dev)
+        _need_packed(w_up, "w_up", (E, h, d), dev)
+        _need_packed(w_down, "w_down", (E, d, h), dev)
         if out is None:
             out = torch.empty((T, d), dtype=torch.float32, device=dev)
         _need(out, "out", "f32", (T, d), dev)
-        fn = _lib.lib.moe_forward_packed if self.packed else _lib.lib.moe_forward
         with torch.cuda.device(dev):
-            _lib.check(fn(ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate),
+            _lib.check(_lib.lib.moe_forward(ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_gate),
                           _ptr(w_up), _ptr(w_down), _ptr(out), _ptr(self.ws), self.ws.numel(), _stream(dev)))
         return out
 
@@ -252,7 +260,8 @@ class MoEForward:
 
 
 def moe_forward(x, w_router, router_bias, w_gate, w_up, w_down, k: int):
-    """One-shot forward (allocates a workspace per call; use MoEForward to reuse one)."""
+    """One-shot forward on packed expert weights (allocates a workspace per call; use MoEForward
+    to reuse one)."""
     T, d = x.shape
     E, h, _ = w_gate.shape
     return MoEForward(T, d, E, k, h, x.device)(x, w_router, router_bias, w_gate, w_up, w_down)
@@ -350,12 +359,10 @@ def moe_combine_rmsnorm(y_rows, row_of, topk_w, gain, eps: float, want_u: bool =
 
 
 class LatentMoEForward:
-    """moe_latent_forward (moe_latent_forward_packed when packed: every bf16 weight passed through
-    moe_pack_weights) with a reusable workspace (allocated once per shape)."""
+    """moe_latent_forward with a reusable workspace (allocated once per shape); every bf16 weight
+    packed (moe_pack_weights)."""
 
-    def __init__(self, T: int, d: int, l: int, E: int, k: int, h: int, n_shared: int, h_shared: int, device,
-                 packed: bool = False):
-        self.packed = packed
+    def __init__(self, T: int, d: int, l: int, E: int, k: int, h: int, n_shared: int, h_shared: int, device):
         self.shape = _lib.latent_shape(T, d, l, E, k, h, n_shared, h_shared)
         self.T, self.d, self.l, self.E, self.k, self.h = T, d, l, E, k, h
         self.S, self.hs = n_shared, h_shared
@@ -370,22 +377,21 @@ class LatentMoEForward:
         _need(w_router, "w_router", "f32", (E, d), dev)
         if router_bias is not None:
             _need(router_bias, "router_bias", "f32", (E,), dev)
-        _need(w_proj_down, "w_proj_down", "bf16", (l, d), dev)
-        _need(w_gate, "w_gate", "bf16", (E, h, l), dev)
-        _need(w_up, "w_up", "bf16", (E, h, l), dev)
-        _need(w_down, "w_down", "bf16", (E, l, h), dev)
+        _need_packed(w_proj_down, "w_proj_down", (l, d), dev)
+        _need_packed(w_gate, "w_gate", (E, h, l), dev)
+        _need_packed(w_up, "w_up", (E, h, l), dev)
+        _need_packed(w_down, "w_down", (E, l, h), dev)
         _need(rms_gain, "rms_gain", "f32", (l,), dev)
-        _need(w_proj_up, "w_proj_up", "bf16", (d, l), dev)
+        _need_packed(w_proj_up, "w_proj_up", (d, l), dev)
         if S > 0:
-            _need(shared_gate, "shared_gate", "bf16", (S, hs, d), dev)
-            _need(shared_up, "shared_up", "bf16", (S, hs, d), dev)
-            _need(shared_down, "shared_down", "bf16", (S, d, hs), dev)
+            _need_packed(shared_gate, "shared_gate", (S, hs, d), dev)
+            _need_packed(shared_up, "shared_up", (S, hs, d), dev)
+            _need_packed(shared_down, "shared_down", (S, d, hs), dev)
         if out is None:
             out = torch.empty((T, d), dtype=torch.float32, device=dev)
         _need(out, "out", "f32", (T, d), dev)
-        fn = _lib.lib.moe_latent_forward_packed if self.packed else _lib.lib.moe_latent_forward
         with torch.cuda.device(dev):
-            _lib.check(fn(
+            _lib.check(_lib.lib.moe_latent_forward(
                 ctypes.byref(self.shape), _ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w_proj_down),
                 _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(rms_gain), rms_eps, _ptr(w_proj_up),
                 _ptr(shared_gate if S > 0 else None), _ptr(shared_up if S > 0 else None),

@@ -94,6 +94,14 @@ def check_layer(out_gpu, out_ref, what="out"):
     return max_rel, mean_abs
 
 
+def packed(*ws):
+    """Row-major bf16 weight tensors converted once to the library's packed layout (moe_pack_weights,
+    on their device): the form every layer call takes."""
+    from sparse_mixture_experts_fp32_amd import moe_pack_weights
+    out = tuple(moe_pack_weights(w) for w in ws)
+    return out if len(out) > 1 else out[0]
+
+
 class LazyExperts:
     """Indexable view of one device weight tensor that copies expert e to the host on demand."""
 

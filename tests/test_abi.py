@@ -40,8 +40,7 @@ def test_header_declares_the_boundary():
               "moe_latent_workspace_bytes", "moe_latent_ws_offset", "moe_combine_rmsnorm",
               "moe_mx_quantize_weights", "moe_mx_quantize_rows", "moe_mx_expert_ffn", "moe_mx_forward",
               "moe_mx_forward_ws_offset", "moe_mx_expert_gate_up", "moe_mx_expert_down",
-              "moe_pack_weights", "moe_expert_gate_up_packed", "moe_expert_down_packed", "moe_forward_packed",
-              "moe_latent_forward_packed"]:
+              "moe_pack_weights", "moe_permute_noalloc"]:
         assert n in names
 
 
@@ -77,7 +76,7 @@ def test_probe_library_exports_its_header():
 
 def test_status_strings(lib):
     L = lib.lib
-    assert L.moe_abi_version() == lib.ABI_VERSION == 9
+    assert L.moe_abi_version() == lib.ABI_VERSION == 10
     assert L.moe_status_str(0) == b"ok"
     for s in range(1, 5):
         assert L.moe_status_str(s) and L.moe_status_str(s) != b"ok"
@@ -314,7 +313,7 @@ def test_mx_calls_check_arguments(lib):
             assert offs[i] + sizes[i] <= offs[i + 1]
 
 
-def test_packed_calls_check_arguments(lib):
+def test_pack_weights_checks_arguments(lib):
     L = lib.lib
     a, b = ctypes.c_void_p(4096), ctypes.c_void_p(8192)
     assert L.moe_pack_weights(2, 24, 128, a, b, None) == 1     # N not a multiple of 16
@@ -323,9 +322,13 @@ def test_packed_calls_check_arguments(lib):
     assert L.moe_pack_weights(2, 32, 128, a, ctypes.c_void_p(4096 + 2 * 32 * 128 * 2 - 16), None) == 1  # overlap
     assert L.moe_pack_weights(2, 32, 128, None, b, None) == 1
     assert L.moe_pack_weights(0, 32, 128, None, None, None) == 0
-    s = _shape(lib)
-    need = lib.workspace_bytes(s, lib.MOE_CALL_FORWARD)
-    assert L.moe_forward_packed(ctypes.byref(s), a, a, None, a, a, a, a, a, need - 1, None) == 3
-    assert L.moe_forward_packed(ctypes.byref(s), a, a, None, None, a, a, a, a, need, None) == 1
-    assert L.moe_expert_gate_up_packed(ctypes.byref(s), a, None, a, a, None, a, a, 1 << 20, None) == 1
-    assert L.moe_expert_down_packed(ctypes.byref(s), a, a, a, a, a, 10, None) == 3
+
+
+def test_one_weight_format(lib):
+    """The layer calls take packed weights; no second, row-major entry point exists."""
+    names = declared_functions()
+    assert not [n for n in names if n.endswith("_packed")], names
+    raw = ctypes.CDLL(LIB)
+    for n in ("moe_forward_packed", "moe_expert_gate_up_packed", "moe_expert_down_packed",
+              "moe_latent_forward_packed"):
+        assert not hasattr(raw, n), n

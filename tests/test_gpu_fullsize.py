@@ -1,12 +1,15 @@
-"""GPU parity at the full workload sizes (one moe_forward call). The oracle
-checks what it can compute in seconds: gate logits of sampled tokens, every
-routing id and weight, the whole permutation, sampled x_perm rows, every H and
-Y row of two experts (a sample of rows for a very large expert), and the layer
-output of sampled tokens computed one by one through their own experts. The
-forward on packed expert weights, the configuration the benchmark times, must
-then give the same output bit for bit."""
-import sys
-
+"""GPU parity at the full workload sizes (one moe_forward call on packed expert
+weights, the configuration the benchmark times). The oracle checks what it can
+compute in seconds:
+  * gate logits of sampled tokens, every routing id and weight, the whole
+    permutation, sampled rows of the standalone x_perm gather;
+  * H and Y rows of the largest expert, the first and last row of every one of
+    its m-tiles (the tile list cuts an expert with M rows into ceil(M / 192)
+    tiles of ceil(M / tiles) rows) plus a random sample, and of one more expert;
+  * the combine of 512 sampled tokens (and the first and last) against host sums
+    of the device's own Y rows, within the float32 sum bound;
+  * the layer output of 8 sampled tokens computed one by one through their own
+    experts by the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -32,8 +35,10 @@ def test_full_size_layer(moe, name):
     print(f"\n[full-size] {cfg}", flush=True)
     inp = make_inputs(cfg, device=dev)
     fwd = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
-    out = fwd(inp.x, inp.w_router, inp.router_bias, inp.w_gate, inp.w_up, inp.w_down)
+    packed = gu.packed(inp.w_gate, inp.w_up, inp.w_down)
+    out = fwd(inp.x, inp.w_router, inp.router_bias, *packed)
     torch.cuda.synchronize()
+    del packed
     rng = np.random.default_rng(cfg.seed)
     x_h = inp.x.cpu()
     wr_h = inp.w_router.cpu()
@@ -57,33 +62,48 @@ def test_full_size_layer(moe, name):
     assert torch.equal(xp[torch.from_numpy(xr).to(dev)].cpu(), x_h[torch.from_numpy(row_src[xr])])
     del xp, rs2
 
-    # every H / Y row of two experts (at most 512 sampled rows of a very large one)
+    # H / Y rows: the largest expert's m-tile edges plus a sample, and one more expert
     nonempty = np.flatnonzero(counts)
-    for e in {int(np.argmax(counts)), int(rng.choice(nonempty))}:
+    big = int(np.argmax(counts))
+    for e in (big, int(rng.choice(nonempty))):
         lo, hi = int(off[e]), int(off[e + 1])
+        m = hi - lo
+        n_tiles = -(-m // 192)
+        per = -(-m // n_tiles)
+        edges = {lo + min(i * per, m - 1) for i in range(n_tiles)} | {lo + min((i + 1) * per, m) - 1
+                                                                      for i in range(n_tiles)}
         sel = np.arange(lo, hi)
         if sel.size > 512:
-            sel = np.sort(rng.choice(sel, size=512, replace=False))
+            sel = rng.choice(sel, size=512, replace=False)
+        sel = np.array(sorted(set(sel.tolist()) | edges))
         X = x_h[torch.from_numpy(row_src[sel])]
         wg, wu, wd = inp.w_gate[e].cpu(), inp.w_up[e].cpu(), inp.w_down[e].cpu()
         H_ref, Y_ref = orc.expert_swiglu(X, wg, wu, wd)
         st = torch.from_numpy(sel).to(dev)
         gu.check_h_rows(fwd.intermediate("h_act")[st].cpu(), H_ref, what=f"H expert {e}")
         gu.check_y_rows(fwd.intermediate("y_rows")[st].cpu(), Y_ref, H_ref, wd, what=f"Y expert {e}")
+        print(f"[full-size] {name}: expert {e}: {len(sel)} of {m} H/Y rows, {n_tiles} m-tile(s), edges included",
+              flush=True)
+
+    # the combine of sampled tokens on the device's own Y rows
+    toks_c = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, size=min(512, cfg.T), replace=False)]))
+    tc = torch.from_numpy(toks_c).to(dev)
+    rows_c = row_of[toks_c]
+    Yc = orc.f64(fwd.intermediate("y_rows")[torch.from_numpy(rows_c.reshape(-1)).to(dev)].cpu()).reshape(
+        len(toks_c), cfg.k, cfg.d)
+    wc = orc.f64(fwd.intermediate("topk_w")[tc].cpu())
+    acc = np.zeros((len(toks_c), cfg.d))
+    for j in range(cfg.k):
+        acc += wc[:, j:j + 1] * Yc[:, j]
+    bound = (cfg.k + 1) * 2.0 ** -23 * np.sum(np.abs(wc)[:, :, None] * np.abs(Yc), axis=1) + 1e-30
+    assert np.all(np.abs(orc.f64(out[tc].cpu()) - acc) <= bound), "combine differs from the host sums"
+    print(f"[full-size] {name}: combine of {len(toks_c)} tokens within the float32 sum bound", flush=True)
 
     # layer output of sampled tokens, each through its own experts
-    toks = np.sort(rng.choice(cfg.T, size=min(4, cfg.T), replace=False))
+    toks = np.sort(rng.choice(cfg.T, size=min(8, cfg.T), replace=False))
     ref = orc.forward(x_h[toks], wr_h, b_h, gu.LazyExperts(inp.w_gate), gu.LazyExperts(inp.w_up),
                       gu.LazyExperts(inp.w_down), cfg.k, logits=logits[toks])
     max_rel, mean_abs = gu.check_layer(out[torch.from_numpy(toks).to(dev)].cpu(), ref["out"])
     print(f"[full-size] {name}: sampled out max rel {max_rel:.2e}, mean abs {mean_abs:.2e}", flush=True)
-    del fwd
-    # the benchmarked configuration: packed expert weights, the same output bit for bit
-    packed = [moe.moe_pack_weights(w) for w in (inp.w_gate, inp.w_up, inp.w_down)]
-    out_p = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev, packed=True)(inp.x, inp.w_router,
-                                                                                inp.router_bias, *packed)
-    torch.cuda.synchronize()
-    assert torch.equal(out_p, out), "packed-weight forward differs from the row-major forward"
-    print(f"[full-size] {name}: packed-weight forward equal bit for bit", flush=True)
-    del packed, out_p, out, inp
+    del fwd, out, inp
     torch.cuda.empty_cache()

@@ -42,11 +42,20 @@ def moe(dev):
     return m
 
 
+def _packed_args(inp):
+    """The layer's arguments after x with every bf16 weight matrix in the packed layout."""
+    wr, b, wpd, wg, wu, wd, gain, eps, wpu, sg, su, sd = inp.args()
+    pk = lambda w: None if w is None else gu.packed(w)  # noqa: E731
+    return wr, b, pk(wpd), pk(wg), pk(wu), pk(wd), gain, eps, pk(wpu), pk(sg), pk(su), pk(sd)
+
+
 def _run(moe, dev, inp):
     c = inp.cfg
     fwd = moe.LatentMoEForward(c.T, c.d, c.l, c.E, c.k, c.h, c.n_shared, c.h_shared, dev)
-    out = fwd(inp.x, *inp.args())
+    args = _packed_args(inp)
+    out = fwd(inp.x, *args)
     torch.cuda.synchronize()
+    fwd.args = args
     return fwd, out
 
 
@@ -140,7 +149,7 @@ def test_latent_forward_deterministic(dev, moe):
     inp = make_latent_inputs(cfg, device=dev, gen_device="cpu")
     fwd, a = _run(moe, dev, inp)
     a = a.clone()
-    b = fwd(inp.x, *inp.args())
+    b = fwd(inp.x, *fwd.args)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 

@@ -252,7 +252,7 @@ def test_expert_ffn_vs_oracle(dev, moe, T, d, E, k, h, skew, gathered):
     off, row_of, row_src = orc.permute(idx, E)
     x_perm = inp.x[torch.from_numpy(row_src)]
     off_d = torch.from_numpy(off.astype(np.int32)).to(dev)
-    w = (inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev))
+    w = gu.packed(inp.w_gate.to(dev), inp.w_up.to(dev), inp.w_down.to(dev))
     if gathered:  # rows read from x through row_src inside the GEMM
         h_act, y_rows = moe.moe_expert_ffn(inp.x.to(dev), off_d, *w, T, k,
                                            a_rows=torch.from_numpy(row_src.astype(np.int32)).to(dev))
@@ -297,7 +297,7 @@ def _forward_and_oracle(moe, dev, inp, cfg, **wover):
     ws = dict(w_gate=g.w_gate, w_up=g.w_up, w_down=g.w_down)
     ws.update({k_: v.to(dev) for k_, v in wover.items()})
     fwd = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
-    out = fwd(g.x, g.w_router, g.router_bias, ws["w_gate"], ws["w_up"], ws["w_down"])
+    out = fwd(g.x, g.w_router, g.router_bias, *gu.packed(ws["w_gate"], ws["w_up"], ws["w_down"]))
     _sync()
     host_w = dict(w_gate=inp.w_gate, w_up=inp.w_up, w_down=inp.w_down)
     host_w.update(wover)
@@ -333,7 +333,7 @@ def test_forward_vs_oracle(dev, moe, base, over):
     off, row_of, row_src, x_perm = moe.moe_permute(g.x, idx, cfg.E)
     _sync()
     assert torch.equal(x_perm.cpu(), inp.x[torch.from_numpy(ref["row_src"])])
-    h_act, y_rows = moe.moe_expert_ffn(x_perm, off, g.w_gate, g.w_up, g.w_down, cfg.T, cfg.k)
+    h_act, y_rows = moe.moe_expert_ffn(x_perm, off, *gu.packed(g.w_gate, g.w_up, g.w_down), cfg.T, cfg.k)
     out2 = moe.moe_combine(y_rows, row_of, w)
     _sync()
     assert torch.equal(out2, out)
@@ -402,12 +402,13 @@ def test_forward_deterministic_and_token_equivariant(dev, moe):
     inp = make_inputs(cfg)
     g = inp.to(dev)
     fwd = moe.MoEForward(cfg.T, cfg.d, cfg.E, cfg.k, cfg.h, dev)
-    a = fwd(g.x, g.w_router, None, g.w_gate, g.w_up, g.w_down).clone()
-    b = fwd(g.x, g.w_router, None, g.w_gate, g.w_up, g.w_down).clone()
+    w = gu.packed(g.w_gate, g.w_up, g.w_down)
+    a = fwd(g.x, g.w_router, None, *w).clone()
+    b = fwd(g.x, g.w_router, None, *w).clone()
     _sync()
     assert torch.equal(a, b), "two runs differ"
     perm = torch.from_numpy(np.random.default_rng(0).permutation(cfg.T)).to(dev)
-    c = fwd(g.x[perm].contiguous(), g.w_router, None, g.w_gate, g.w_up, g.w_down)
+    c = fwd(g.x[perm].contiguous(), g.w_router, None, *w)
     _sync()
     assert torch.equal(c, a[perm]), "permuting tokens does not permute the output rows"
 
@@ -415,7 +416,7 @@ def test_forward_deterministic_and_token_equivariant(dev, moe):
 def test_forward_zero_tokens(dev, moe):
     fwd = moe.MoEForward(0, 128, 8, 2, 256, dev)
     inp = make_inputs(CONFIGS["tiny"]).to(dev)
-    out = fwd(torch.empty(0, 128, dtype=torch.bfloat16, device=dev), inp.w_router, None, inp.w_gate, inp.w_up,
-              inp.w_down)
+    out = fwd(torch.empty(0, 128, dtype=torch.bfloat16, device=dev), inp.w_router, None,
+              *gu.packed(inp.w_gate, inp.w_up, inp.w_down))
     _sync()
     assert out.shape == (0, 128)
