@@ -410,7 +410,7 @@ def mx_bench(args, lib, inp, cfg, dev, note):
                          "mfma_frac_fp8": flops / ((gate_up_ms + down_ms) * 1e-3) / 1e12 / 5000.0,
                          "gate_up_ms": gate_up_ms, "h_quantise_ms": hq_ms, "down_ms": down_ms,
                          "down_gbs": dn_bytes / (down_ms * 1e-3) / 1e9},
-        "roofline": {"kernel": "mx_grouped_kernel<gated> (MX gate/up pass + SwiGLU)", "bound": "hbm",
+        "roofline": {"kernel": "mx_ring_kernel<gated> (MX gate/up pass + SwiGLU)", "bound": "hbm",
                      "achieved": gu_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gu_gbs / HBM_PEAK_GBS,
                      "traffic": None, "algorithmic_bytes": gu_bytes},
     }

@@ -20,6 +20,11 @@ static __device__ __forceinline__ void dma_saddr(uint32_t lds, const void* sbase
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
                  : "memory", "m0");
 }
+// sbase + voff -> LDS, 4 bytes per lane (lane l writes LDS byte lds + 4 l)
+static __device__ __forceinline__ void dma_saddr_dword(uint32_t lds, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
 // a 64-bit address per lane -> LDS
 static __device__ __forceinline__ void dma_vaddr(uint32_t lds, const void* addr) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(addr)

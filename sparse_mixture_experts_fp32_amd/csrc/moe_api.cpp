@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -220,6 +221,10 @@ int check_mx_shape(const moe_shape_t* s) {
     if (s->d % 512 != 0 || s->h % 512 != 0)
         return fail(MOE_ERR_UNSUPPORTED, "the MX path needs d and h to be multiples of 512 (d = %d, h = %d)", s->d,
                     s->h);
+    const int64_t n = s->T * static_cast<int64_t>(s->k);
+    if (n * std::max(s->d, s->h) >= (int64_t(1) << 32))
+        return fail(MOE_ERR_UNSUPPORTED, "the MX path addresses its E4M3 rows with 32-bit offsets: T * k * max(d, h) = %lld "
+                    ">= 2^32", static_cast<long long>(n * std::max(s->d, s->h)));
     return MOE_OK;
 }
 

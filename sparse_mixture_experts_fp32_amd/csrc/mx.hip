@@ -138,154 +138,238 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__
 
 // --------------------------------------------------------- grouped GEMM
 //
-// Work unit and schedule as in the bf16 grouped GEMM (m-tiles of one expert
-// from the device-built tile list, here of up to 128 rows, n-tiles of the
-// weight rows, m-tiles of one expert innermost within each XCD's contiguous
-// share). Workgroup: 8 wavefronts; each owns four 16-row blocks of weight rows
-// (gate and up rows of the same 32 outputs for the gate/up pass, 64 output rows
-// for the down pass) and every row of the m-tile, so each 32-byte A fragment
-// read from LDS feeds four matrix instructions. Per K step of 128: the A rows (128
-// bytes each) and their four scale bytes are staged in LDS, double-buffered;
-// each lane loads its 16 bytes of E2M1 weights per block straight into
-// registers (one kilobyte per wavefront, contiguous) three steps ahead, and one
-// scale word per block every four steps.
-
+// Work unit and schedule as in the bf16 ring kernel (m-tiles of one expert from
+// the device-built tile list, here of up to 144 rows; n-tiles of the weight
+// rows; the m-tiles that share an expert's n-tile side by side on one XCD).
+// Workgroup: 8 wavefronts; each owns four 16-row blocks of weight rows (gate
+// and up rows of the same 32 outputs for the gate/up pass, 64 output rows for
+// the down pass) and every row of the m-tile, so each 32-byte A fragment read
+// from LDS feeds four matrix instructions.
+//
+// Operands reach LDS through direct-to-LDS loads into a ring of three stages,
+// one K step of 128 each:
+//   * A rows (E4M3): per 16-row block two loads of 1 KiB, the first holding
+//     bytes 0..63 of each row's K step, the second bytes 64..127, lane l at
+//     byte 16 l as the fragment reads want them (row l % 16, bytes 16 (l / 16)
+//     of each half); the row's scale word (its four block scales for the step)
+//     at word r;
+//   * weights (E2M1): one contiguous kilobyte per block and step, permuted on
+//     the way so that lane l's 16 bytes land at byte 16 l;
+//   * weight scales: one 256-byte group per block and four steps, in a region
+//     of each wave's own, loaded with the step that first needs it.
+// A wave's weight region of a slot is its own, so its weight loads for step
+// s + 3 go out as soon as it has finished reading step s, before the next
+// barrier; the shared A rows for step s + 2 go out after the barrier that
+// starts step s. The waits are exact counts of the loads issued after the
+// ones a step needs (vector-memory counters retire in issue order), so a step
+// never waits for later stages.
 constexpr int kMxWaves = 8;
 constexpr int kMxThreads = kMxWaves * 64;
-constexpr int kMxNB = 4;
-constexpr int kMxKS = 128;
-constexpr int kMxMaxMB = 8;
-constexpr int kMxBM = 16 * kMxMaxMB;
-constexpr int kMxARow = kMxKS + 32;  // LDS bytes per staged row: 32 B of padding keeps the 16-byte
-                                     // fragment reads of 16 rows conflict-free (16 B measured 39 %
-                                     // of LDS-active cycles in bank conflicts)
-constexpr int kMxRowsPerPass = kMxThreads / (kMxKS / 16);
-static_assert(kMxBM % kMxRowsPerPass == 0, "whole staging passes");
+constexpr int kMxNB = 4;                                 // 16-row weight blocks per wave
+constexpr int kMxStages = 3;
+constexpr int kMxMaxMB = 9;                              // 16-row A blocks per m-tile (144 rows)
+constexpr int kMxAStage = kMxMaxMB * 2048;               // A rows of one step
+constexpr int kMxWStage = kMxWaves * kMxNB * 1024;       // weight rows of one step
+constexpr int kMxSStage = 16 * kMxMaxMB * 4;             // A scale words of one step
+constexpr int kMxStage = kMxAStage + kMxWStage + kMxSStage;
+constexpr int kMxWSOff = kMxStages * kMxStage;           // weight scale groups, 1 KiB per wave
+constexpr int kMxLds = kMxWSOff + kMxWaves * 1024;
+static_assert(kMxLds <= 160 * 1024, "the ring fits one CU's LDS");
+constexpr int kMxAInstMax = (2 * kMxMaxMB + kMxWaves - 1) / kMxWaves;  // A loads per wave and step, at most
+constexpr int kMxSInst = (16 * kMxMaxMB + 63) / 64;      // scale-word loads per step (the last one partial)
 
 template <int kSel>
 __device__ __forceinline__ f32x4 mfma_e4m3_e2m1(const v8i& a, const v8i& b, const f32x4& c, int sa, int sb) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 4, 0, sa, kSel, sb);
 }
 
-template <bool kGated, int kMB>
-__device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t* __restrict__ A,
-                                        const uint8_t* __restrict__ As, const int32_t* __restrict__ A_rows,
-                                        int64_t A_nrows, int64_t row0, int M, const uint8_t* const (&wq)[kMxNB],
-                                        const uint8_t* const (&wsc)[kMxNB], uint32_t lane_q, uint32_t lane_s,
-                                        bool wave_on, int N, int K, int n_wave,
-                                        float* __restrict__ C) {
-    constexpr int kPasses = (16 * kMB + kMxRowsPerPass - 1) / kMxRowsPerPass;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int fr = lane & 15, fg = lane >> 4;
-    const int nb = K / kMxBlock;
+// Wait until at most n (wave-uniform, 0..15) of this wave's vector-memory
+// operations are in flight and its LDS operations are done, then barrier.
+__device__ __forceinline__ void mx_wait_barrier(int n) {
+    switch (n) {
+        case 0: wait_barrier<0>(); break;
+        case 1: wait_barrier<1>(); break;
+        case 2: wait_barrier<2>(); break;
+        case 3: wait_barrier<3>(); break;
+        case 4: wait_barrier<4>(); break;
+        case 5: wait_barrier<5>(); break;
+        case 6: wait_barrier<6>(); break;
+        case 7: wait_barrier<7>(); break;
+        case 8: wait_barrier<8>(); break;
+        case 9: wait_barrier<9>(); break;
+        case 10: wait_barrier<10>(); break;
+        case 11: wait_barrier<11>(); break;
+        case 12: wait_barrier<12>(); break;
+        case 13: wait_barrier<13>(); break;
+        case 14: wait_barrier<14>(); break;
+        default: wait_barrier<15>(); break;
+    }
+}
 
-    // staging: thread -> (row, 16-byte chunk); the first 16 * kMB threads also move a scale word
-    const int a_row = tid / (kMxKS / 16), a_chunk = tid % (kMxKS / 16);
-    int64_t a_off[kPasses];
+// Keep each step's matrix instructions inside the step: an empty volatile asm
+// that reads and rewrites every accumulator (it emits no instruction).
+template <int kMB>
+__device__ __forceinline__ void pin_acc(f32x4 (&acc)[kMxNB][kMB]) {
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-        const int64_t r = row0 + min(p * kMxRowsPerPass + a_row, M - 1);
-        const int64_t src = A_rows ? min(max(static_cast<int64_t>(A_rows[r]), int64_t(0)), A_nrows - 1) : r;
-        a_off[p] = src * K + a_chunk * 16;
+    for (int j = 0; j < kMxNB; ++j)
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) asm volatile("" : "+v"(acc[j][i]));
+}
+
+// One K step from one ring slot: acc[j][i] += A block i x weight block j, scale
+// byte kSel of the weight scale words (a word covers four steps). Fragment i + 1
+// is read while fragment i multiplies; the fences keep that order.
+template <int kMB, int kSel>
+__device__ __forceinline__ void mx_step(f32x4 (&acc)[kMxNB][kMB], const uint8_t* a_lds, const uint32_t* s_lds,
+                                        const uint8_t* w_lds, uint32_t (&ws)[kMxNB], const uint32_t* ws_lds,
+                                        int fg) {
+    if (kSel == 0) {
+#pragma unroll
+        for (int j = 0; j < kMxNB; ++j) ws[j] = ws_lds[64 * j];
     }
-    const bool s_on = tid < 16 * kMB;
-    int64_t s_off;
+    v8i b[kMxNB];
+#pragma unroll
+    for (int j = 0; j < kMxNB; ++j) {
+        const u32x4 t = *reinterpret_cast<const u32x4*>(w_lds + 1024 * j);
+        b[j] = v8i{static_cast<int>(t.x), static_cast<int>(t.y), static_cast<int>(t.z), static_cast<int>(t.w), 0, 0,
+                   0, 0};
+    }
+    u32x4 lo[2], hi[2];
+    uint32_t sw[2];
+    lo[0] = *reinterpret_cast<const u32x4*>(a_lds);
+    hi[0] = *reinterpret_cast<const u32x4*>(a_lds + 1024);
+    sw[0] = s_lds[0];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kMB; ++i) {
+        if (i + 1 < kMB) {
+            lo[(i + 1) % 2] = *reinterpret_cast<const u32x4*>(a_lds + 2048 * (i + 1));
+            hi[(i + 1) % 2] = *reinterpret_cast<const u32x4*>(a_lds + 2048 * (i + 1) + 1024);
+            sw[(i + 1) % 2] = s_lds[16 * (i + 1)];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const u32x4 l = lo[i % 2], h = hi[i % 2];
+        const v8i a = v8i{static_cast<int>(l.x), static_cast<int>(l.y), static_cast<int>(l.z), static_cast<int>(l.w),
+                          static_cast<int>(h.x), static_cast<int>(h.y), static_cast<int>(h.z), static_cast<int>(h.w)};
+        const int sa = static_cast<int>(sw[i % 2] >> (8 * fg));
+#pragma unroll
+        for (int j = 0; j < kMxNB; ++j)
+            acc[j][i] = mfma_e4m3_e2m1<kSel>(a, b[j], acc[j][i], sa, static_cast<int>(ws[j]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+template <bool kGated, int kMB>
+__device__ __forceinline__ void mx_tile(uint8_t* lds, const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
+                                        const int32_t* __restrict__ A_rows, int64_t A_nrows, int64_t row0, int M,
+                                        const uint8_t* const (&wq)[kMxNB], const uint8_t* const (&wsc)[kMxNB], int N,
+                                        int K, int n_out, float* __restrict__ C) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int fr = lane & 15, fg = lane >> 4;
+    const uint32_t base = lds_addr(lds);
+    const int nb = K / kMxBlock;
+    const int nk = K / kMxKStep;  // a multiple of 4
+
+    // A loads q = wave, wave + 8, wave + 16 (while q < 2 kMB): block q / 2, half q % 2;
+    // lane l reads row 16 (q / 2) + l % 16 (clamped to the tile, gathered through
+    // A_rows), bytes 64 (q % 2) + 16 (l / 16) of the step. Offsets are 32-bit (A
+    // holds fewer than 2^32 bytes; the launcher checks).
+    constexpr int kAInst = 2 * kMB;
+    int nA = 0;
+    uint32_t a_off[kMxAInstMax];
+#pragma unroll
+    for (int p = 0; p < kMxAInstMax; ++p) {
+        const int q = min(wave + kMxWaves * p, kAInst - 1);
+        nA += wave + kMxWaves * p < kAInst ? 1 : 0;
+        const int64_t r = row0 + min(16 * (q / 2) + fr, M - 1);
+        const int64_t src = A_rows ? min(max(static_cast<int64_t>(A_rows[r]), int64_t(0)), A_nrows - 1) : r;
+        a_off[p] = static_cast<uint32_t>(src * K + 64 * (q % 2) + 16 * fg);
+    }
+    // scale-word loads p = 0 .. kMxSInst - 1 by waves 7, 6, ...: lane l moves the word of
+    // row 64 p + l (the last load only for the rows that exist in a full tile)
+    const int ps = kMxWaves - 1 - wave;
+    const bool s_on = ps < kMxSInst;
+    const bool s_part = ps == kMxSInst - 1 && (16 * kMxMaxMB) % 64 != 0;
+    uint32_t s_off;
     {
-        const int64_t r = row0 + min(tid, M - 1);
+        const int64_t r = row0 + min(64 * min(ps, kMxSInst - 1) + lane, M - 1);
         const int64_t src = A_rows ? min(max(static_cast<int64_t>(A_rows[r]), int64_t(0)), A_nrows - 1) : r;
-        s_off = src * nb;
+        s_off = static_cast<uint32_t>(src * nb);
     }
-    constexpr int kBufA = kMxBM * kMxARow, kBufS = kMxBM;
+    // weight scale groups: lane l moves bytes 16 (l % 16) of block l / 16's group
+    const int lb = lane >> 4;
+    const uint8_t* ws_src = (lb == 0 ? wsc[0] : lb == 1 ? wsc[1] : lb == 2 ? wsc[2] : wsc[3]) + 16 * (lane & 15);
+    const uint32_t lane_q = 64u * fr + 16u * fg;  // weights: lane l reads its fragment's 16 bytes
+    const int nAS = nA + (s_on ? 1 : 0);
+
+    auto issue_a = [&](int s) {  // A rows and their scale words of step s (after the barrier)
+        const uint32_t slot = base + static_cast<uint32_t>((s % kMxStages) * kMxStage);
+        if (s_on) {
+            const uint32_t dst = slot + kMxAStage + kMxWStage + 256u * ps;
+            if (!s_part)
+                dma_saddr_dword(dst, As, s_off + 4u * s);
+            else if (lane < 16 * kMxMaxMB - 64 * (kMxSInst - 1))
+                dma_saddr_dword(dst, As, s_off + 4u * s);
+        }
+#pragma unroll
+        for (int p = 0; p < kMxAInstMax; ++p)
+            if (p < nA) dma_saddr(slot + 1024u * (wave + kMxWaves * p), A, a_off[p] + 128u * s);
+    };
+    auto issue_w = [&](int s) {  // this wave's weights (and scale group) of step s
+        const uint32_t slot = base + static_cast<uint32_t>((s % kMxStages) * kMxStage);
+        if (s % 4 == 0) dma_vaddr(base + kMxWSOff + 1024u * wave, ws_src + 256 * (s / 4));
+        const uint32_t wslot = slot + kMxAStage + 4096u * wave;
+#pragma unroll
+        for (int j = 0; j < kMxNB; ++j) dma_saddr(wslot + 1024u * j, wq[j], lane_q + 1024u * s);
+    };
+    // loads issued after the A rows of step s: W(s + 1), A(s + 1), W(s + 2)
+    auto after_a = [&](int s) {
+        int n = 0;
+        if (s + 1 < nk) n += kMxNB + ((s + 1) % 4 == 0 ? 1 : 0) + nAS;
+        if (s + 2 < nk) n += kMxNB + ((s + 2) % 4 == 0 ? 1 : 0);
+        return n;
+    };
 
     f32x4 acc[kMxNB][kMB];
 #pragma unroll
-    for (int b = 0; b < kMxNB; ++b)
+    for (int j = 0; j < kMxNB; ++j)
 #pragma unroll
-        for (int i = 0; i < kMB; ++i) acc[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < kMB; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / kMxKS;  // a multiple of 4
-    u32x4 ar[2][kPasses];      // A rows, two K steps ahead
-    uint32_t sr[2] = {0u, 0u}; // their scale words
-    auto load_a = [&](u32x4 (&dst)[kPasses], uint32_t& sdst, int s) {
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p) dst[p] = *reinterpret_cast<const u32x4*>(A + a_off[p] + s * kMxKS);
-        if (s_on) sdst = *reinterpret_cast<const uint32_t*>(As + s_off + s * 4);
-    };
-    auto store_a = [&](int buf, const u32x4 (&src)[kPasses], uint32_t ssrc) {
-#pragma unroll
-        for (int p = 0; p < kPasses; ++p)
-            *reinterpret_cast<u32x4*>(sA + buf * kBufA + (p * kMxRowsPerPass + a_row) * kMxARow + a_chunk * 16) =
-                src[p];
-        if (s_on) sS[buf * kBufS + tid] = ssrc;
-    };
-    u32x4 bq[4][kMxNB];        // weights, a ring of four K steps (three ahead)
-    uint32_t bs[2][kMxNB];     // weight scale words, two sets of four K steps
-    auto load_b = [&](u32x4 (&dst)[kMxNB], int s) {
-#pragma unroll
-        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const u32x4*>(wq[b] + (lane_q + s * 1024u));
-    };
-    auto load_bs = [&](uint32_t (&dst)[kMxNB], int q4) {
-#pragma unroll
-        for (int b = 0; b < kMxNB; ++b) dst[b] = *reinterpret_cast<const uint32_t*>(wsc[b] + (lane_s + q4 * 256u));
-    };
-    // multiply one K step from LDS buffer `buf` with weights w and scale byte sel of words ws
-    auto step = [&](int buf, const u32x4 (&w)[kMxNB], const uint32_t (&ws)[kMxNB], auto sel) {
-        constexpr int kSel = decltype(sel)::value;
-        v8i bop[kMxNB];
-#pragma unroll
-        for (int b = 0; b < kMxNB; ++b) bop[b] = v8i{static_cast<int>(w[b].x), static_cast<int>(w[b].y),
-                                                    static_cast<int>(w[b].z), static_cast<int>(w[b].w), 0, 0, 0, 0};
-        const uint8_t* arow = sA + buf * kBufA + fr * kMxARow + 16 * fg;
-        const uint32_t* srow = sS + buf * kBufS + fr;
-#pragma unroll
-        for (int i = 0; i < kMB; ++i) {
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(arow + i * 16 * kMxARow);
-            const u32x4 hi = *reinterpret_cast<const u32x4*>(arow + i * 16 * kMxARow + 64);
-            const v8i aop = v8i{static_cast<int>(lo.x), static_cast<int>(lo.y), static_cast<int>(lo.z),
-                                static_cast<int>(lo.w), static_cast<int>(hi.x), static_cast<int>(hi.y),
-                                static_cast<int>(hi.z), static_cast<int>(hi.w)};
-            const int sa = static_cast<int>(srow[i * 16] >> (8 * fg));
-#pragma unroll
-            for (int b = 0; b < kMxNB; ++b)
-                acc[b][i] = mfma_e4m3_e2m1<kSel>(aop, bop[b], acc[b][i], sa, static_cast<int>(ws[b]));
-        }
-    };
-
-    load_a(ar[0], sr[0], 0);
-    load_a(ar[1], sr[1], min(1, nk - 1));
-    load_b(bq[0], 0);
-    load_b(bq[1], min(1, nk - 1));
-    load_b(bq[2], min(2, nk - 1));
-    load_bs(bs[0], 0);
-    store_a(0, ar[0], sr[0]);
-    __syncthreads();
-    // Eight steps per trip (every register index a compile-time constant): steps
-    // 0-3 use scale word set 0 (word s0 / 4), steps 4-7 set 1 (word s0 / 4 + 1),
-    // each set loaded four steps before it is used. Step U: load A rows of step
-    // s + 2, then weights of step s + 3 (vector-memory counters retire in issue
-    // order, so waiting for the A rows of s + 1 never waits for later weights),
-    // multiply step s (scale byte U % 4), store the A rows of s + 1 in the other
-    // LDS buffer, barrier.
-#define MOE_MX_STEP(U, SET)                                                                           \
-    {                                                                                                 \
-        const int s = s0 + (U);                                                                       \
-        load_a(ar[(U) % 2], sr[(U) % 2], min(s + 2, nk - 1));                                         \
-        load_b(bq[((U) + 3) % 4], min(s + 3, nk - 1));                                                \
-        if (wave_on) step((U) % 2, bq[(U) % 4], bs[SET], std::integral_constant<int, (U) % 4>{});     \
-        store_a(((U) + 1) % 2, ar[((U) + 1) % 2], sr[((U) + 1) % 2]);                                 \
-        __syncthreads();                                                                              \
+    issue_w(0);
+    issue_a(0);
+    if (nk > 1) {
+        issue_w(1);
+        issue_a(1);
     }
-    for (int s0 = 0; s0 < nk; s0 += 8) {
-        load_bs(bs[1], min(s0 / 4 + 1, nk / 4 - 1));
-        MOE_MX_STEP(0, 0) MOE_MX_STEP(1, 0) MOE_MX_STEP(2, 0) MOE_MX_STEP(3, 0)
-        if (s0 + 4 < nk) {  // uniform
-            load_bs(bs[0], min(s0 / 4 + 2, nk / 4 - 1));
-            MOE_MX_STEP(4, 1) MOE_MX_STEP(5, 1) MOE_MX_STEP(6, 1) MOE_MX_STEP(7, 1)
-        }
+    if (nk > 2) issue_w(2);
+    const uint8_t* a_lds = lds + 16 * lane;
+    const uint32_t* s_lds = reinterpret_cast<const uint32_t*>(lds + kMxAStage + kMxWStage) + fr;
+    const uint8_t* w_lds = lds + kMxAStage + 4096 * wave + 16 * lane;
+    const uint32_t* ws_lds = reinterpret_cast<const uint32_t*>(lds + kMxWSOff + 1024 * wave + 16 * fr + 4 * fg);
+    uint32_t ws[kMxNB];
+    // Step U of a group of four: wait for step s's loads, barrier (every wave is
+    // done with step s - 1), issue the A rows of s + 2 into the slot s - 1 used,
+    // multiply, then issue this wave's weights of s + 3 into the slot it just read.
+#define MOE_MX_STEP(U)                                                                                 \
+    {                                                                                                  \
+        const int s = s0 + (U);                                                                        \
+        mx_wait_barrier(after_a(s));                                                                   \
+        if (s + 2 < nk) issue_a(s + 2);                                                                \
+        const int off = (s % kMxStages) * kMxStage;                                                    \
+        mx_step<kMB, (U)>(acc, a_lds + off, s_lds + off / 4, w_lds + off, ws, ws_lds, fg);             \
+        pin_acc(acc);                                                                                  \
+        if (s + 3 < nk) {                                                                              \
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");                                         \
+            issue_w(s + 3);                                                                            \
+        }                                                                                              \
+    }
+    for (int s0 = 0; s0 < nk; s0 += 4) {
+        MOE_MX_STEP(0) MOE_MX_STEP(1) MOE_MX_STEP(2) MOE_MX_STEP(3)
     }
 #undef MOE_MX_STEP
 
-    if (!wave_on) return;
     // Every value first, then the stores back to back: a store reads its data and
     // address registers after issue, so interleaving each store with the next
     // value's arithmetic would make the compiler wait for every store to finish.
@@ -300,7 +384,7 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
                     acc[c][i][qq] = g / (1.0f + __expf(-g)) * u;
                 }
     }
-    float* cbase = C + row0 * N + n_wave + fr;
+    float* cbase = C + row0 * N + n_out + fr;
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
 #pragma unroll
@@ -319,17 +403,18 @@ __device__ __forceinline__ void mx_tile(uint8_t* sA, uint32_t* sS, const uint8_t
     }
 }
 
+// One workgroup per CU (157 KiB of LDS), so the register allocator may give each
+// of the two waves per SIMD half the register file.
 template <bool kGated>
 __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(1, 2)))
-void mx_grouped_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
-                       const int32_t* __restrict__ A_rows, int64_t A_nrows, const int4* __restrict__ tiles,
-                       const int32_t* __restrict__ tile_start, int E, int n_tiles, const uint8_t* __restrict__ W0q,
-                       const uint8_t* __restrict__ W0s, const uint8_t* __restrict__ W1q,
-                       const uint8_t* __restrict__ W1s, int N, int K, float* __restrict__ C) {
-    constexpr int kColsW = kGated ? 16 * kMxNB / 2 : 16 * kMxNB;
+void mx_ring_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const int32_t* __restrict__ A_rows,
+                    int64_t A_nrows, const int4* __restrict__ tiles, const int32_t* __restrict__ tile_start, int E,
+                    int n_tiles, const uint8_t* __restrict__ W0q, const uint8_t* __restrict__ W0s,
+                    const uint8_t* __restrict__ W1q, const uint8_t* __restrict__ W1s, int N, int K,
+                    float* __restrict__ C) {
+    constexpr int kColsW = kGated ? 16 * kMxNB / 2 : 16 * kMxNB;  // output columns per wave
     constexpr int kColsWG = kColsW * kMxWaves;
-    __shared__ __attribute__((aligned(16))) uint8_t sA[2 * kMxBM * kMxARow];
-    __shared__ uint32_t sS[2 * kMxBM];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kMxLds];
 
     const int n_mt = tile_start[E];
     const int xcd = blockIdx.x % kXcdsMx;
@@ -349,11 +434,8 @@ void mx_grouped_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
     if (M <= 0) return;
     const int64_t row0 = tile.y;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int n_wave = nt * kColsWG + wave * kColsW;
-    const bool wave_on = n_wave < N;
-    const int n_safe = wave_on ? n_wave : 0;
-    const int fr = lane & 15, fg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n_out = nt * kColsWG + wave * kColsW;  // N is a multiple of kColsWG: every wave has columns
     const int64_t wrows = static_cast<int64_t>(e) * N;  // first weight row of expert e
     // each block's tile row (16 weight rows) starts at a wave-uniform address; a lane's operand
     // sits at a fixed offset inside every 1 KiB tile (and every 256-byte scale group)
@@ -364,29 +446,31 @@ void mx_grouped_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict_
         const bool up = kGated && b >= kMxNB / 2;  // gate/up: blocks 0 .. kMxNB / 2 - 1 gate, then up
         const uint8_t* q = up ? W1q : W0q;
         const uint8_t* s = up ? W1s : W0s;
-        const int64_t n0 = wrows + n_safe + 16 * (kGated ? b % (kMxNB / 2) : b);  // a multiple of 16
+        const int64_t n0 = wrows + n_out + 16 * (kGated ? b % (kMxNB / 2) : b);  // a multiple of 16
         wq[b] = static_cast<const uint8_t*>(uniform_ptr(q + wcode_offset(n0, 0, K)));
         wsc[b] = static_cast<const uint8_t*>(uniform_ptr(s + wscale_offset(n0, 0, K)));
     }
-    const uint32_t lane_q = 64u * fr + 16u * fg;  // K step s: + s * 1024
-    const uint32_t lane_s = 16u * fr + 4u * fg;   // four K steps q4: + q4 * 256
-    const int mb = min(kMxMaxMB, (M + 31) / 32 * 2);  // 2, 4, 6 or 8 blocks
-#define MOE_MX_TILE(NB)                                                                                   \
-    if (mb == (NB)) {                                                                                     \
-        mx_tile<kGated, (NB)>(sA, sS, A, As, A_rows, A_nrows, row0, M, wq, wsc, lane_q, lane_s, wave_on, N, K, n_wave, \
-                              C);                                                                         \
-        return;                                                                                           \
+    const int mb = min(kMxMaxMB, (M + 15) / 16);
+#define MOE_MX_TILE(NB)                                                                                  \
+    if (mb == (NB)) {                                                                                    \
+        mx_tile<kGated, (NB)>(lds, A, As, A_rows, A_nrows, row0, M, wq, wsc, N, K, n_out, C);           \
+        return;                                                                                          \
     }
+    MOE_MX_TILE(1)
     MOE_MX_TILE(2)
+    MOE_MX_TILE(3)
     MOE_MX_TILE(4)
+    MOE_MX_TILE(5)
     MOE_MX_TILE(6)
+    MOE_MX_TILE(7)
     MOE_MX_TILE(8)
+    MOE_MX_TILE(9)
 #undef MOE_MX_TILE
 }
 
 // ---------------------------------------------------------------- launchers
 
-int mx_tile_rows() { return kMxBM; }
+int mx_tile_rows() { return 16 * kMxMaxMB; }
 
 hipError_t launch_mx_quantize(const void* in, bool in_f32, int64_t rows, int K, bool fp4, uint8_t* q,
                               uint8_t* scales, hipStream_t stream) {
@@ -412,16 +496,17 @@ hipError_t launch_mx_ffn_pass(bool gated, const uint8_t* a, const uint8_t* a_sca
                               const uint8_t* w0q, const uint8_t* w0s, const uint8_t* w1q, const uint8_t* w1s, int N,
                               int K, float* c, hipStream_t stream) {
     const int cols_wg = (gated ? 16 * kMxNB / 2 : 16 * kMxNB) * kMxWaves;
-    const int n_tiles = (N + cols_wg - 1) / cols_wg;
+    // whole n-tiles, whole groups of four K steps, 32-bit A offsets
+    if (N % cols_wg != 0 || K % (4 * kMxKStep) != 0 || a_nrows * K >= (int64_t(1) << 32)) return hipErrorInvalidValue;
+    const int n_tiles = N / cols_wg;
     const int slots = (ffn_max_tiles(n_rows, E) + kXcdsMx - 1) / kXcdsMx;
     const int64_t grid = static_cast<int64_t>(kXcdsMx) * slots * n_tiles;
     if (gated)
-        hipLaunchKernelGGL((mx_grouped_kernel<true>), dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0, stream,
-                           a, a_scales, a_rows, a_nrows, tiles, tile_start, E, n_tiles, w0q, w0s, w1q, w1s, N, K, c);
+        hipLaunchKernelGGL((mx_ring_kernel<true>), dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0, stream, a,
+                           a_scales, a_rows, a_nrows, tiles, tile_start, E, n_tiles, w0q, w0s, w1q, w1s, N, K, c);
     else
-        hipLaunchKernelGGL((mx_grouped_kernel<false>), dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0,
-                           stream, a, a_scales, a_rows, a_nrows, tiles, tile_start, E, n_tiles, w0q, w0s, w0q, w0s, N,
-                           K, c);
+        hipLaunchKernelGGL((mx_ring_kernel<false>), dim3(static_cast<unsigned>(grid)), dim3(kMxThreads), 0, stream, a,
+                           a_scales, a_rows, a_nrows, tiles, tile_start, E, n_tiles, w0q, w0s, w0q, w0s, N, K, c);
     return hipGetLastError();
 }
 

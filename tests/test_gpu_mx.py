@@ -186,6 +186,8 @@ CASES = {
     "many_tiles": dict(T=700, d=512, E=3, k=2, h=1024),
     "empty_experts": dict(T=20, d=512, E=64, k=1, h=512),
     "k_equals_E": dict(T=9, d=512, E=4, k=4, h=512),
+    "tile_144": dict(T=144, d=512, E=2, k=2, h=512),    # one full m-tile of 144 rows per expert
+    "tiles_135": dict(T=270, d=1024, E=2, k=2, h=512),  # two m-tiles of 135 rows (nine 16-row blocks)
 }
 
 
