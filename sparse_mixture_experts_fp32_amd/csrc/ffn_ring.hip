@@ -37,10 +37,14 @@
 //    packed weights each weight load is one contiguous kilobyte of HBM.
 //  * One barrier per K step: wait for this wave's loads of step i (vmcnt),
 //    barrier (now every wave's step-i A rows are in LDS, and every wave is done
-//    with step i - 1), issue the loads of step i + 2 into the slot step i - 1
-//    used, multiply step i. The waits are written out (the compiler does not
-//    track LDS writes of these loads precisely and would otherwise drain every
-//    load at every barrier).
+//    with step i - 1), issue the A rows of step i + 2 into the slot step i - 1
+//    used, multiply step i. A wave's weight region of a slot is its own, so it
+//    issues its weight loads of step i + 3 as soon as it has finished reading
+//    step i, without waiting for the other waves. The waits are exact counts
+//    of the loads issued after the ones step i needs (vector-memory counters
+//    retire in issue order) and are written out: the compiler does not track
+//    LDS writes of these loads precisely and would otherwise drain every load
+//    at every barrier.
 //
 // Packed weight layout (moe_pack_weights): matrix [N, K] as tiles of 16 rows x
 // 32 columns, 512 elements each, in (row block, column block) order; inside a
@@ -62,6 +66,36 @@ constexpr int kRAStage = kRMaxMB * 1024;             // bytes of A rows per stag
 constexpr int kRWStage = kRWaves * kRNB * 1024;      // bytes of weight rows per stage
 constexpr int kRStage = kRAStage + kRWStage;         // 44 KiB
 constexpr int kRFragAhead = 4;                       // A fragments read ahead of their MFMAs
+
+// Wait until at most n (wave-uniform, 0..12) of this wave's vector-memory
+// operations are in flight and its LDS operations are done, then barrier.
+__device__ __forceinline__ void ring_wait_barrier(int n) {
+    switch (n) {
+        case 0: wait_barrier<0>(); break;
+        case 1: wait_barrier<1>(); break;
+        case 2: wait_barrier<2>(); break;
+        case 3: wait_barrier<3>(); break;
+        case 4: wait_barrier<4>(); break;
+        case 5: wait_barrier<5>(); break;
+        case 6: wait_barrier<6>(); break;
+        case 7: wait_barrier<7>(); break;
+        case 8: wait_barrier<8>(); break;
+        case 9: wait_barrier<9>(); break;
+        case 10: wait_barrier<10>(); break;
+        case 11: wait_barrier<11>(); break;
+        default: wait_barrier<12>(); break;
+    }
+}
+
+// Keep each step's matrix instructions inside the step: an empty volatile asm
+// that reads and rewrites every accumulator (it emits no instruction).
+template <int kMB>
+__device__ __forceinline__ void ring_pin(f32x4 (&acc)[kRNB][kMB]) {
+#pragma unroll
+    for (int j = 0; j < kRNB; ++j)
+#pragma unroll
+        for (int i = 0; i < kMB; ++i) asm volatile("" : "+v"(acc[j][i]));
+}
 
 // acc[j][i] += A block i (from LDS) x weight block j (from LDS), one K step.
 template <int kMB>
@@ -115,17 +149,18 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
     const uint32_t w_lane = 16u * lane;
     constexpr uint32_t kWStep = 1024u;  // bytes per K step
 
-    auto issue = [&](int s) {  // loads of K step s into ring slot s % 3
+    auto issue_a = [&](int s) {  // A rows of K step s into ring slot s % 3
         const uint32_t slot = ring_lds + static_cast<uint32_t>((s % kRStages) * kRStage);
 #pragma unroll
         for (int p = 0; p < 2; ++p)
             if (p < nA) dma_vaddr(slot + 1024u * (wave + kRWaves * p), a_src[p] + kRKS * s);
-        if (wave_on) {
-            const uint32_t wslot = slot + kRAStage + 1024u * kRNB * wave;
-            const uint32_t voff = w_lane + kWStep * s;
+    };
+    auto issue_w = [&](int s) {  // this wave's weight rows of K step s
+        const uint32_t wslot = ring_lds + static_cast<uint32_t>((s % kRStages) * kRStage) + kRAStage +
+                               1024u * kRNB * wave;
+        const uint32_t voff = w_lane + kWStep * s;
 #pragma unroll
-            for (int j = 0; j < kRNB; ++j) dma_saddr(wslot + 1024u * j, wblk[j], voff);
-        }
+        for (int j = 0; j < kRNB; ++j) dma_saddr(wslot + 1024u * j, wblk[j], voff);
     };
 
     f32x4 acc[kRNB][kMB];
@@ -135,30 +170,40 @@ __device__ __forceinline__ void ring_tile(uint8_t* ring, const uint16_t* __restr
         for (int i = 0; i < kMB; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / kRKS;
-    issue(0);
-    if (nk > 1) issue(1);
     // One K loop per wave role (the branch stays outside the loop, so the
-    // accumulators never pass through a merge point inside it). Step s needs this
-    // wave's loads of step s done while step s + 1's may stay in flight.
+    // accumulators never pass through a merge point inside it).
     if (!wave_on) {  // loads A rows for the others (nA per step), multiplies nothing
+        issue_a(0);
+        if (nk > 1) issue_a(1);
         for (int s = 0; s < nk; ++s) {
             wait_loads_barrier(s + 1 < nk ? nA : 0);
-            if (s + 2 < nk) issue(s + 2);
+            if (s + 2 < nk) issue_a(s + 2);
         }
         return;
     }
-    // an active wave issues its A rows before its kRNB weight loads, so "at most
-    // kRNB in flight" means step s is complete (and step s + 1's A rows too)
+    // Issue order W(0) A(0) W(1) A(1) W(2), then per step s: A(s + 2) after the
+    // barrier, W(s + 3) after the multiply; so the loads issued after A(s) are
+    // W(s + 1), A(s + 1) and W(s + 2), and waiting until only those are in flight
+    // completes step s (W(s) went out before A(s)).
+    issue_w(0);
+    issue_a(0);
+    if (nk > 1) {
+        issue_w(1);
+        issue_a(1);
+    }
+    if (nk > 2) issue_w(2);
     const uint8_t* a_lds = ring + 16 * lane;
     const uint8_t* w_lds = ring + kRAStage + 1024 * kRNB * wave + 16 * lane;
     for (int s = 0; s < nk; ++s) {
-        if (s + 1 < nk)
-            wait_barrier<kRNB>();
-        else
-            wait_barrier<0>();
-        if (s + 2 < nk) issue(s + 2);
+        ring_wait_barrier((s + 1 < nk ? kRNB + nA : 0) + (s + 2 < nk ? kRNB : 0));
+        if (s + 2 < nk) issue_a(s + 2);
         const int off = (s % kRStages) * kRStage;
         ring_mfma<kMB>(acc, a_lds + off, w_lds + off);
+        ring_pin(acc);
+        if (s + 3 < nk) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this wave is done reading slot s % 3
+            issue_w(s + 3);
+        }
     }
 #pragma unroll
     for (int i = 0; i < kMB; ++i) {
