@@ -706,6 +706,17 @@ def main():
         print(json.dumps({"ceilings": measure_ceilings(dev, note),
                           "peaks": {"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}}), flush=True)
         return
+    if args.copy_probe_mib > 0:
+        # a plain float32 copy (out = -in) of known size, whose L2-to-fabric counters
+        # calibrate those of the layer's kernels in the same profiled run
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
+        print("[bench] copy probe done", file=sys.stderr, flush=True)
     if args.workload in LATENT_CONFIGS:
         note = lambda msg: print(f"[bench] {args.workload}: {msg}", file=sys.stderr, flush=True)  # noqa: E731
         print(json.dumps(latent_bench(args, dev, note)), flush=True)
@@ -736,16 +747,6 @@ def main():
     note("expert weights packed into matrix-core tiles")
     layer = Layer(lib, inp, cfg, dev, weights)
     note("buffers allocated")
-
-    if args.copy_probe_mib > 0:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            torch.neg(a, out=b)
-        torch.cuda.synchronize()
-        del a, b
-        note("copy probe done")
 
     for _ in range(args.warmup):
         layer.step()
