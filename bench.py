@@ -45,7 +45,7 @@ METRIC = "MoE-layer tokens/s + grouped-GEMM TFLOP/s (% MFMA peak), d=7168 E=256 
 # a hash of the kernel's sources: reported only while those sources are unchanged.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_{workload}.json")
 PROBE_LIB = os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "libmoe_probe.so")
-FLUSH_BYTES = 512 << 20  # written between cold-cache calls: twice the last-level cache
+FLUSH_BYTES = 512 << 20  # read between cold-cache calls: twice the last-level cache
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
@@ -148,31 +148,50 @@ def time_hbm_kernels(layer, reps):
         lambda: c(L.moe_permute(sh, P(layer.inp.x), P(layer.idx), P(layer.offsets), P(layer.row_of),
                                 P(layer.row_src), P(x_perm), P(layer.ws_perm), layer.ws_perm.numel(), sp)),
         4.0 * T * k + 4.0 * (E + 1) + 8.0 * T * k + 2.0 * T * d + 2.0 * T * k * d, "hbm")
-    out = {"reps": reps, "cold": f"{FLUSH_BYTES >> 20} MiB scratch written before each cold call"}
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=layer.dev)
+    out = {"reps": reps, "cold": f"{FLUSH_BYTES >> 20} MiB of scratch read before each cold call (a read evicts the "
+                                  "caches with clean lines; a written flush leaves dirty lines whose write-back "
+                                  "would be timed with the call)"}
+    probe = ctypes.CDLL(PROBE_LIB)
+    probe.moe_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=layer.dev)
+    tiles_out = torch.empty(FLUSH_BYTES // 32768 + 1, dtype=torch.int32, device=layer.dev)
 
-    def timed(cold):
+    def timed(fn, cold):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for i, (a, b) in enumerate(evs):
+        for a, b in evs:
             if cold:
-                flush.fill_(float(i))
+                probe.moe_probe_read_tiles(P(flush), FLUSH_BYTES, P(tiles_out), sp)
             a.record(layer.stream)
-            call()
+            fn()
             b.record(layer.stream)
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
 
+    # a size-matched reference: the one-pass read probe (libmoe_probe.so) over as many bytes as
+    # the call moves, timed the same way, shows what one launch of that size reaches on this chip
     for name, (call, nbytes, bound) in calls.items():
         for _ in range(3):
             call()
-        us, us_cold = timed(False), timed(True)
+        us, us_cold = timed(call, False), timed(call, True)
         gbs, gbs_cold = nbytes / (us * 1e-6) / 1e9, nbytes / (us_cold * 1e-6) / 1e9
         rec = {"us": us, "us_cold": us_cold, "bytes": nbytes, "gbs": gbs, "gbs_cold": gbs_cold,
                "hbm_frac": gbs / HBM_PEAK_GBS, "hbm_frac_cold": gbs_cold / HBM_PEAK_GBS, "bound": bound}
         if bound == "hbm":  # the >= 70 % of HBM target, judged on the cold rate
             rec["target_70pct_met"] = gbs_cold / HBM_PEAK_GBS >= 0.70
+            nb = int(nbytes) // 16 * 16
+            buf = torch.ones(nb // 4, dtype=torch.float32, device=layer.dev)
+            rout = torch.empty(nb // 32768 + 1, dtype=torch.int32, device=layer.dev)
+            read = lambda: probe.moe_probe_read_tiles(P(buf), nb, P(rout), sp)  # noqa: E731
+            for _ in range(3):
+                read()
+            r_us, r_us_cold = timed(read, False), timed(read, True)
+            del buf, rout
+            rec["plain_read_same_bytes"] = {"us": r_us, "us_cold": r_us_cold, "gbs": nb / (r_us * 1e-6) / 1e9,
+                                            "gbs_cold": nb / (r_us_cold * 1e-6) / 1e9,
+                                            "hbm_frac_cold": nb / (r_us_cold * 1e-6) / 1e9 / HBM_PEAK_GBS}
+            rec["frac_of_plain_read_cold"] = r_us_cold / us_cold
         out[name] = rec
-    del flush
+    del flush, tiles_out
     return out
 
 

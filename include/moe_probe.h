@@ -11,6 +11,10 @@
  * check exactly, so that a probe cannot be fast by skipping its work:
  *  - moe_probe_read: sink[0] += the sum, modulo 2^32, of every 32-bit word of
  *    buf (plain 16-byte vector loads into registers);
+ *  - moe_probe_read_tiles: one pass without atomics: out[b] = the sum, modulo
+ *    2^32, of the words of the b-th 32 KiB tile of buf (the last one may be
+ *    partial), each workgroup issuing all its loads at once; the read of a
+ *    buffer of tens of MB in one launch, the size of the layer's small kernels;
  *  - moe_probe_dma_read: the same sum, with buf streamed by direct-to-LDS loads
  *    (global_load_lds_dwordx4, the load of the expert GEMM's LDS ring) through
  *    a three-stage LDS ring, then read back from LDS;
@@ -33,6 +37,8 @@ extern "C" {
 
 /* bytes a multiple of 16 */
 int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+/* bytes a multiple of 16; out [ceil(bytes / 32768)] */
+int moe_probe_read_tiles(const void* buf, size_t bytes, uint32_t* out, void* stream);
 /* bytes a multiple of 32768 (one ring stage) */
 int moe_probe_dma_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 /* bytes a multiple of 16; src and dst do not overlap */

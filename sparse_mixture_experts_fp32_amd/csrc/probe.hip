@@ -18,10 +18,42 @@ constexpr int kDmaStage = 32768;  // 8 waves x 4 loads of 1 KiB
 
 __device__ __forceinline__ uint32_t word_sum(const u32x4& v) { return v.x + v.y + v.z + v.w; }
 
+// One atomic per workgroup (one per wave would serialise thousands of atomics on
+// one address and dominate the time of a small probe).
 __device__ __forceinline__ void add_to_sink(uint32_t acc, uint32_t* sink) {
+    __shared__ uint32_t part[16];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-    if ((threadIdx.x & 63) == 0) atomicAdd(sink, acc);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+        for (int w = 0; w < static_cast<int>(blockDim.x) / kWave; ++w) t += part[w];
+        atomicAdd(sink, t);
+    }
+}
+
+// One pass over the buffer: workgroup b reads 32 KiB tile b (256 threads x eight 16-byte
+// loads, all issued before any is summed; the last tile may be partial) and writes
+// out[b] = the sum of its words modulo 2^32. No loop and no atomic, so a buffer of tens
+// of MB is read as fast as one launch can read it.
+constexpr int kTileChunks = 8 * 256;  // 16-byte chunks per tile
+__global__ __launch_bounds__(256) void probe_read_tiles_kernel(const u32x4* __restrict__ p, int64_t n,
+                                                               uint32_t* __restrict__ out) {
+    __shared__ uint32_t part[4];
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kTileChunks + threadIdx.x;
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = p[min(base + 256 * j, n - 1)];
+    uint32_t acc = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (base + 256 * j < n) acc += word_sum(v[j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
 }
 
 // Each wave reads contiguous 4 KiB runs (four 1 KiB loads in flight, lane l at 16 l of
@@ -134,6 +166,16 @@ extern "C" int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink, voi
     hipLaunchKernelGGL(probe_read_kernel, dim3(probe_grid() * kProbeBlocksPerCu), dim3(kProbeThreads), 0,
                        static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf),
                        static_cast<int64_t>(bytes / 16), sink);
+    return static_cast<int>(hipGetLastError());
+}
+
+extern "C" int moe_probe_read_tiles(const void* buf, size_t bytes, uint32_t* out, void* stream) {
+    if (buf == nullptr || out == nullptr || !aligned16(buf) || bytes % 16 != 0 || bytes == 0) return -1;
+    const int64_t n = static_cast<int64_t>(bytes / 16);
+    const int64_t tiles = (n + kTileChunks - 1) / kTileChunks;
+    if (tiles > 0x7fffffff) return -1;
+    hipLaunchKernelGGL(probe_read_tiles_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), n, out);
     return static_cast<int>(hipGetLastError());
 }
 

@@ -60,7 +60,7 @@ def test_probe_library_exports_its_header():
     path = os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "libmoe_probe.so")
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_[a-z_]+)\s*\(", text, flags=re.M)))
-    assert names == ["moe_probe_copy", "moe_probe_dma_read", "moe_probe_mfma", "moe_probe_read"]
+    assert names == ["moe_probe_copy", "moe_probe_dma_read", "moe_probe_mfma", "moe_probe_read", "moe_probe_read_tiles"]
     L = ctypes.CDLL(path)
     for n in names:
         assert hasattr(L, n), n
@@ -68,6 +68,8 @@ def test_probe_library_exports_its_header():
     sz = ctypes.c_size_t
     assert L.moe_probe_read(None, sz(16), a, None) == -1
     assert L.moe_probe_read(a, sz(15), a, None) == -1
+    assert L.moe_probe_read_tiles(a, sz(24), a, None) == -1       # not a multiple of 16
+    assert L.moe_probe_read_tiles(a, sz(16), None, None) == -1
     assert L.moe_probe_dma_read(a, sz(16), a, None) == -1          # not a whole 32 KiB stage
     assert L.moe_probe_copy(a, ctypes.c_void_p(4096 + 16), sz(64), None) == -1  # overlapping
     assert L.moe_probe_mfma(6, 10, a, None) == -1                  # waves not a multiple of 4

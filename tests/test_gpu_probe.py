@@ -1,7 +1,7 @@
 """GPU test of the ceiling probes (libmoe_probe.so): each does the work it is timed
 for. The read and direct-to-LDS read return the exact sum of the buffer's 32-bit
-words, the copy reproduces its source, and the matrix-core loop the exact sum of
-its all-ones products."""
+words, the one-pass tile read the sum of each 32 KiB tile, the copy reproduces its
+source, and the matrix-core loop the exact sum of its all-ones products."""
 import ctypes
 import os
 
@@ -20,6 +20,7 @@ def probe():
     L = ctypes.CDLL(os.path.join(ROOT, "sparse_mixture_experts_fp32_amd", "libmoe_probe.so"))
     for n in ("moe_probe_read", "moe_probe_dma_read"):
         getattr(L, n).argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    L.moe_probe_read_tiles.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     L.moe_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     L.moe_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     return L
@@ -45,6 +46,22 @@ def test_read_probes_sum_every_word(probe, nbytes):
         assert fn(_p(buf), nbytes, _p(sink), None) == 0
         torch.cuda.synchronize()
         assert int(sink.cpu().numpy().astype(np.uint32)[0]) == want
+
+
+@pytest.mark.parametrize("nbytes", [16, 32768 * 3 + 48, 60817408])
+def test_read_tiles_probe_sums_each_tile(probe, nbytes):
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(nbytes % 997)
+    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, generator=g).to(dev)
+    tiles = -(-nbytes // 32768)
+    out = torch.zeros(tiles + 1, dtype=torch.int32, device=dev)
+    assert probe.moe_probe_read_tiles(_p(buf), nbytes, _p(out), None) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.uint32)
+    for b in {0, tiles // 2, tiles - 1}:
+        assert int(got[b]) == _word_sum(buf[b * 8192:(b + 1) * 8192]), f"tile {b}"
+    assert int(got[tiles]) == 0, "wrote past the last tile"
+    assert int(got[:tiles].astype(np.uint64).sum() % (1 << 32)) == _word_sum(buf)
 
 
 def test_copy_probe_copies(probe):
