@@ -66,8 +66,8 @@ static int max_tiles_for(int64_t n_rows, int E, int bm) {
 // m-tiles of up to 192 rows: 12 blocks of 16 rows, what one LDS-ring workgroup multiplies
 int ffn_tile_rows() { return 192; }
 
-// Capacity of a tile list: enough for the shortest m-tiles any pass uses (the MX
-// passes' 128 rows), so one workspace serves every pass.
+// Capacity of a tile list: enough for m-tiles of 128 rows, shorter than any pass uses
+// (bf16 192 rows, MX 144), so one workspace serves every pass.
 constexpr int kMinTileRows = 128;
 int ffn_max_tiles(int64_t n_rows, int E) { return max_tiles_for(n_rows, E, kMinTileRows); }
 

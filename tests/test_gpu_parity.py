@@ -1,7 +1,7 @@
 """GPU parity: every step of the HIP path against the CPU oracle, through the C ABI.
 
-Sizes span several tiles with ragged tails (T not a multiple of the 64-token
-gate tile, E not a multiple of 64, experts with more rows than one 128-row
+Sizes span several tiles with ragged tails (T not a multiple of the gate GEMM's
+256-token tile, E not a multiple of 64, experts with more rows than one 192-row
 m-tile, empty experts) plus the degenerate cases (T = 1, E = k = 1, k = E).
 """
 import math
@@ -233,11 +233,12 @@ def test_permute_skips_out_of_range_ids(dev, moe):
 # -------------------------------------------------------------- expert FFN
 
 FFN_CASES = [
-    # (T, d, E, k, h, skew): skew sends every token to expert 0 -> T rows, several 128-row m-tiles
+    # (T, d, E, k, h, skew): skew sends every token to expert 0 -> T rows, several 192-row m-tiles
     (64, 128, 8, 2, 256, False),
     (300, 256, 12, 4, 384, False),
     (37, 384, 5, 2, 128, True),
     (260, 128, 3, 1, 128, True),
+    (600, 256, 3, 1, 256, True),   # 600 rows on expert 0: four m-tiles of 150 rows
     (1, 256, 4, 2, 256, False),
     (129, 512, 64, 8, 256, False),
 ]
