@@ -436,7 +436,9 @@ int moe_combine_rmsnorm(const moe_shape_t* shape, const float* y_rows, const int
  * all-zero block, clamped to [-127, 127]); each element is v / 2^s rounded to
  * the nearest element value, ties to the even code, clamped to the largest
  * value (6 or 448); a value that rounds to zero keeps its sign.
- * The MX calls need d and h to be multiples of 512.
+ * The MX calls need d and h to be multiples of 512, and T * k * max(d, h) < 2^32
+ * (the grouped GEMM addresses its MXFP8 rows with 32-bit offsets); other shapes
+ * return MOE_ERR_UNSUPPORTED.
  *
  * Layouts:
  *  - MXFP4 weights of G matrices [N, K] (N a multiple of 16), in matrix-core

@@ -288,6 +288,10 @@ def test_mx_calls_check_arguments(lib):
     s = _shape(lib, d=256, h=512)
     assert L.moe_mx_forward(ctypes.byref(s), a, a, None, a, a, a, a, a, a, a, a, 1 << 30, None) == 2
     assert L.moe_workspace_bytes(ctypes.byref(s), lib.MOE_CALL_MX_FORWARD) == 0
+    # the MX grouped GEMM addresses its MXFP8 rows with 32-bit offsets: T * k * max(d, h) < 2^32
+    s = _shape(lib, T=1 << 20, d=4096, h=512, E=8, k=1)
+    assert L.moe_mx_expert_gate_up(ctypes.byref(s), a, a, None, a, a, a, a, a, a, a, 1 << 20, None) == 2
+    assert L.moe_mx_expert_down(ctypes.byref(s), a, a, a, a, a, a, a, 1 << 20, None) == 2
     s = _shape(lib, d=512, h=512)
     need = lib.workspace_bytes(s, lib.MOE_CALL_MX_FORWARD)
     assert need > 0 and need % 256 == 0
