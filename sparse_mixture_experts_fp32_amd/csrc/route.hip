@@ -30,24 +30,31 @@ namespace moe {
 // count padded to a multiple of 16 with zero rows, so that one direct-to-LDS
 // load brings one operand.
 //
-// router_gemm_kernel: 256 tokens x 128 experts per 512-thread workgroup; wave
-// (wm, wn) owns 64 tokens x 64 experts (16 accumulator blocks, each fed by the
-// three parts), so every fragment read from LDS feeds 4 or 12 MFMAs. x rows and
-// weight parts go straight into a 3-stage LDS ring. The traffic of such a GEMM
-// is x once per expert block plus the weights once per token block, so the
-// tile is tall in tokens (the three parts weigh three x rows). K is split into
-// S ranges when the token x expert tiles alone would leave CUs idle (a
-// decode-sized batch has one token block): each range writes a float32 partial
-// sum and router_reduce_kernel adds the S partials in range order (and the
-// bias), so the result does not depend on scheduling. The workgroups of one
-// (token block, K range) are dealt to one XCD back to back, so its x rows come
-// from HBM once.
+// router_gemm_kernel<kBM, kWM, kSt>: kBM tokens x 128 experts per 512-thread
+// workgroup, the 8 waves as kWM token rows x (8 / kWM) expert columns, each
+// wave owning 8 x 16 tokens and 128 / (8 / kWM) experts, so every fragment read
+// from LDS feeds between 6 and 12 MFMAs. x rows and weight parts go straight
+// into an LDS ring of kSt stages (one K step of 32 each; the weight loads of a
+// step are issued before its x rows). Two shapes:
+//  * 256 tokens, waves 2 x 4, three stages (two in flight while one is
+//    multiplied): batches of up to a few thousand tokens;
+//  * 512 tokens, waves 4 x 2, two stages: once the token x expert tiles alone
+//    fill the CUs, the taller tile carries half the weight bytes per MFMA, which
+//    matters more there than a second stage in flight.
+// Each step reads the 3 x (experts / 16) weight fragments and the first x
+// fragment, then reads x fragment i + 1 while fragment i multiplies
+// (scheduling fences keep that order). The traffic of such a GEMM is x once per
+// expert block plus the weights once per token block, so the tile is tall in
+// tokens (the three parts weigh three x rows). K is split into S ranges when
+// the token x expert tiles alone would leave CUs idle (a decode-sized batch has
+// one token block): each range writes a float32 partial sum and
+// router_reduce_kernel adds the S partials in range order (and the bias), so
+// the result does not depend on scheduling. The workgroups of one (token block,
+// K range) are dealt to one XCD back to back, so its x rows come from HBM once.
 
-constexpr int kRtBM = 256, kRtBN = 128, kRtKS = 32, kRtStages = 3;
-constexpr int kRtAStage = (kRtBM / 16) * 1024;        // 16 KiB of x rows per stage
+constexpr int kRtBN = 128, kRtKS = 32;
 constexpr int kRtBStage = 3 * (kRtBN / 16) * 1024;    // 24 KiB of weight parts per stage
-constexpr int kRtStage = kRtAStage + kRtBStage;       // 40 KiB
-constexpr int kRtLoads = kRtStage / 1024 / 8;         // loads per wave per stage (5)
+constexpr int kRtNB = kRtBStage / 1024 / 8;           // weight-part loads per wave per stage (3)
 
 static __host__ __device__ int router_epad(int E) { return (E + 15) / 16 * 16; }
 
@@ -95,12 +102,41 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float* __restri
     }
 }
 
+// Wait until at most n (wave-uniform, 0..5) of this wave's vector-memory operations are in flight
+// and its LDS operations are done, then barrier.
+__device__ __forceinline__ void router_wait_barrier(int n) {
+    switch (n) {
+        case 0: wait_barrier<0>(); break;
+        case 1: wait_barrier<1>(); break;
+        case 2: wait_barrier<2>(); break;
+        case 3: wait_barrier<3>(); break;
+        case 4: wait_barrier<4>(); break;
+        default: wait_barrier<5>(); break;
+    }
+}
+
+// Keep each step's matrix instructions inside the step: an empty volatile asm that reads and
+// rewrites every accumulator (it emits no instruction).
+template <int kMI, int kNJ>
+__device__ __forceinline__ void router_pin(f32x4 (&acc)[kMI][kNJ]) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) asm volatile("" : "+v"(acc[i][j]));
+}
+
 // out: logits [T, E] (+ bias) when n_split == 1, else partial sums [n_split][T][E].
+template <int kBM, int kWM, int kSt>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2)))
 void router_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ parts,
                         const float* __restrict__ bias, float* __restrict__ out, int64_t T, int d, int E,
                         int n_mblocks, int n_nblocks, int n_split) {
-    __shared__ __attribute__((aligned(1024))) uint8_t ring[kRtStages * kRtStage];
+    constexpr int kWN = 8 / kWM;
+    constexpr int kMI = kBM / kWM / 16, kNJ = kRtBN / kWN / 16;  // 16 x 16 blocks per wave
+    constexpr int kAStage = (kBM / 16) * 1024;                   // x rows per stage
+    constexpr int kStage = kAStage + kRtBStage;
+    constexpr int kNA = kBM / 16 / 8;                            // x-row loads per wave per stage
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kSt * kStage];
     // (token block m, K range r) pairs go to XCD (block id % 8) in turn, each with its expert blocks in a row
     const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
     const int pair = 8 * (j / n_nblocks) + xcd, nblk = j % n_nblocks;
@@ -108,9 +144,9 @@ void router_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
     const int mblk = pair / n_split, range = pair % n_split;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave & 3, wn = wave >> 2;
+    const int wm = wave % kWM, wn = wave / kWM;
     const int frag_row = lane & 15, frag_k = 8 * (lane >> 4);
-    const int64_t m0 = static_cast<int64_t>(mblk) * kRtBM;
+    const int64_t m0 = static_cast<int64_t>(mblk) * kBM;
     const int n0 = nblk * kRtBN;
     const int eblocks = router_epad(E) / 16;
     const int64_t pn = static_cast<int64_t>(eblocks) * 16 * d;
@@ -120,77 +156,91 @@ void router_gemm_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
     const int s_hi = static_cast<int>(static_cast<int64_t>(range + 1) * nk_all / n_split);
     const int nk = s_hi - s_lo;  // >= 1: n_split <= nk_all
 
-    // this wave's loads per stage: x row blocks 2 wave, 2 wave + 1 (lane: row, K 8 (l / 16));
-    // weight blocks 3 wave .. 3 wave + 2 of the 24 (part p = idx / 8, expert block idx % 8)
-    const uint16_t* a_src[2];
+    // this wave's loads per stage: x row blocks wave + 8 p (lane: row, K 8 (l / 16)); weight blocks
+    // wave + 8 q of the 24 (part idx / 8, expert block idx % 8)
+    const uint16_t* a_src[kNA];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        const int64_t row = min(m0 + 16 * (2 * wave + p) + frag_row, T - 1);
+    for (int p = 0; p < kNA; ++p) {
+        const int64_t row = min(m0 + 16 * (wave + 8 * p) + frag_row, T - 1);
         a_src[p] = x + row * d + frag_k + kRtKS * s_lo;
     }
-    const uint16_t* b_src[3];
+    const uint16_t* b_src[kRtNB];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int idx = 3 * wave + q;
+    for (int q = 0; q < kRtNB; ++q) {
+        const int idx = wave + 8 * q;
         const int eb = min(n0 / 16 + idx % 8, eblocks - 1);  // clamped: such columns are never stored
         b_src[q] = static_cast<const uint16_t*>(
             uniform_ptr(parts + (idx / 8) * pn + (static_cast<int64_t>(eb) * (d / 32) + s_lo) * 512));
     }
-    auto issue = [&](int s) {  // local step s of this K range into ring slot s % kRtStages
-        const uint32_t slot = ring_lds + static_cast<uint32_t>((s % kRtStages) * kRtStage);
+    auto issue = [&](int s) {  // local step s of this K range into ring slot s % kSt
+        const uint32_t slot = ring_lds + static_cast<uint32_t>((s % kSt) * kStage);
 #pragma unroll
-        for (int p = 0; p < 2; ++p) dma_vaddr(slot + 1024u * (2 * wave + p), a_src[p] + kRtKS * s);
+        for (int q = 0; q < kRtNB; ++q)
+            dma_saddr(slot + kAStage + 1024u * (wave + 8 * q), b_src[q], 16u * lane + 1024u * s);
 #pragma unroll
-        for (int q = 0; q < 3; ++q) dma_saddr(slot + kRtAStage + 1024u * (3 * wave + q), b_src[q], 16u * lane + 1024u * s);
+        for (int p = 0; p < kNA; ++p) dma_vaddr(slot + 1024u * (wave + 8 * p), a_src[p] + kRtKS * s);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[kMI][kNJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMI; ++i)
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int jn = 0; jn < kNJ; ++jn) acc[i][jn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    issue(0);
-    if (nk > 1) issue(1);
-    const uint8_t* a_lds = ring + 1024 * (4 * wm) + 16 * lane;
-    const uint8_t* b_lds = ring + kRtAStage + 1024 * (4 * wn) + 16 * lane;
+#pragma unroll
+    for (int s = 0; s < kSt - 1; ++s)
+        if (s < nk) issue(s);
+    const uint8_t* a_lds = ring + 1024 * (kMI * wm) + 16 * lane;
+    const uint8_t* b_lds = ring + kAStage + 1024 * (kNJ * wn) + 16 * lane;
     for (int s = 0; s < nk; ++s) {
-        // step s has landed once only step s + 1's loads (if any) are in flight
-        if (s + 1 < nk)
-            wait_barrier<kRtLoads>();
-        else
-            wait_barrier<0>();
-        if (s + 2 < nk) issue(s + 2);
-        const int off = (s % kRtStages) * kRtStage;
-        bf16x8 b[3][4];
+        // step s has landed once only the later steps' loads (at most kSt - 2 of them) are in flight
+        router_wait_barrier((kNA + kRtNB) * min(kSt - 2, nk - 1 - s));
+        if (s + kSt - 1 < nk) issue(s + kSt - 1);
+        const int off = (s % kSt) * kStage;
+        bf16x8 b[3][kNJ];
 #pragma unroll
         for (int q = 0; q < 3; ++q)
 #pragma unroll
-            for (int jn = 0; jn < 4; ++jn)
+            for (int jn = 0; jn < kNJ; ++jn)
                 b[q][jn] = *reinterpret_cast<const bf16x8*>(b_lds + off + 1024 * (8 * q + jn));
+        bf16x8 a[2];
+        a[0] = *reinterpret_cast<const bf16x8*>(a_lds + off);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(a_lds + off + 1024 * i);
+        for (int i = 0; i < kMI; ++i) {
+            if (i + 1 < kMI) a[(i + 1) & 1] = *reinterpret_cast<const bf16x8*>(a_lds + off + 1024 * (i + 1));
 #pragma unroll
-            for (int jn = 0; jn < 4; ++jn) {
-                acc[i][jn] = mfma_16x16x32(a, b[2][jn], acc[i][jn]);  // smallest part first
-                acc[i][jn] = mfma_16x16x32(a, b[1][jn], acc[i][jn]);
-                acc[i][jn] = mfma_16x16x32(a, b[0][jn], acc[i][jn]);
+            for (int jn = 0; jn < kNJ; ++jn) {
+                acc[i][jn] = mfma_16x16x32(a[i & 1], b[2][jn], acc[i][jn]);  // smallest part first
+                acc[i][jn] = mfma_16x16x32(a[i & 1], b[1][jn], acc[i][jn]);
+                acc[i][jn] = mfma_16x16x32(a[i & 1], b[0][jn], acc[i][jn]);
             }
         }
+        // the weight fragments and x fragment 0 first, then x fragment i + 1 after the first MFMA of i
+        __builtin_amdgcn_sched_group_barrier(0x100, 3 * kNJ + 1, 0);
+#pragma unroll
+        for (int i = 0; i < kMI; ++i) {
+            if (i + 1 < kMI) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 3 * kNJ - 1, 0);
+            } else {
+                __builtin_amdgcn_sched_group_barrier(0x008, 3 * kNJ, 0);
+            }
+        }
+        router_pin(acc);
     }
 
     float* dst = n_split == 1 ? out : out + static_cast<int64_t>(range) * T * E;
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn) {
-        const int col = n0 + 64 * wn + 16 * jn + frag_row;
+    for (int jn = 0; jn < kNJ; ++jn) {
+        const int col = n0 + (kRtBN / kWN) * wn + 16 * jn + frag_row;
         if (col >= E) continue;
         const float bcol = (n_split == 1 && bias) ? bias[col] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kMI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t row = m0 + 64 * wm + 16 * i + 4 * (lane >> 4) + q;
+                const int64_t row = m0 + (kBM / kWM) * wm + 16 * i + 4 * (lane >> 4) + q;
                 if (row < T) dst[row * E + col] = acc[i][jn][q] + bcol;
             }
     }
@@ -257,19 +307,28 @@ __global__ __launch_bounds__(256) void topk_softmax_kernel(const float* __restri
 
 // ------------------------------------------------------------------ launchers
 
-// K ranges: enough (token block, expert block, K range) workgroups to give most
-// CUs one, at most 32 ranges (their partial sums are read back once more), never
-// a range shorter than one K step.
-static int router_split_count(int64_t T, int d, int E) {
-    const int64_t tiles = ((T + kRtBM - 1) / kRtBM) * ((E + kRtBN - 1) / kRtBN);
-    int64_t s = (256 + tiles - 1) / tiles;
-    if (tiles >= 192) s = 1;
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(s, 32), d / kRtKS)));
+// Tile height and K ranges. 512-token tiles once the 256-token tiles fill the CUs without a K
+// split and the taller tiles take no more rounds of the 256 CUs (counted in 256-token tile
+// work). Otherwise 256-token tiles with K split into S ranges: enough (token block, expert block,
+// K range) workgroups to give most CUs one, at most 32 ranges (their partial sums are read back
+// once more), never a range shorter than one K step.
+struct RouterPlan {
+    int bm, split;
+};
+static RouterPlan router_plan(int64_t T, int d, int E) {
+    const int64_t nb = (E + kRtBN - 1) / kRtBN;
+    const int64_t t256 = ((T + 255) / 256) * nb, t512 = ((T + 511) / 512) * nb;
+    if (t256 >= 192) {
+        if ((t512 + 255) / 256 * 2 <= (t256 + 255) / 256) return {512, 1};
+        return {256, 1};
+    }
+    const int64_t s = (256 + t256 - 1) / t256;
+    return {256, static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(s, 32), d / kRtKS)))};
 }
 
 size_t router_ws_bytes(int64_t T, int d, int E) {
     const size_t parts = sizeof(uint16_t) * 3 * static_cast<size_t>(router_epad(E)) * d;
-    const int S = router_split_count(T, d, E);
+    const int S = router_plan(T, d, E).split;
     const size_t partial = S > 1 ? sizeof(float) * static_cast<size_t>(S) * static_cast<size_t>(T) * E : 0;
     return (parts + 255) / 256 * 256 + partial;
 }
@@ -285,13 +344,19 @@ hipError_t launch_router_gemm(const uint16_t* x, const float* w, const float* bi
     const int64_t blocks = std::min<int64_t>((chunks + 255) / 256, 4096);
     hipLaunchKernelGGL(router_split_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, w, E,
                        router_epad(E), d, parts);
-    const int S = router_split_count(T, d, E);
-    const int n_mblocks = static_cast<int>((T + kRtBM - 1) / kRtBM);
+    const RouterPlan plan = router_plan(T, d, E);
+    const int S = plan.split;
+    const int n_mblocks = static_cast<int>((T + plan.bm - 1) / plan.bm);
     const int n_nblocks = (E + kRtBN - 1) / kRtBN;
     const int64_t pairs = static_cast<int64_t>(n_mblocks) * S;
-    const int64_t grid = static_cast<int64_t>(8) * ((pairs + 7) / 8) * n_nblocks;
-    hipLaunchKernelGGL(router_gemm_kernel, dim3(static_cast<unsigned>(grid)), dim3(512), 0, stream, x, parts, bias,
-                       S == 1 ? logits : partial, T, d, E, n_mblocks, n_nblocks, S);
+    const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(8) * ((pairs + 7) / 8) * n_nblocks));
+    float* dst = S == 1 ? logits : partial;
+    if (plan.bm == 512)
+        hipLaunchKernelGGL((router_gemm_kernel<512, 4, 2>), grid, dim3(512), 0, stream, x, parts, bias, dst, T, d, E,
+                           n_mblocks, n_nblocks, S);
+    else
+        hipLaunchKernelGGL((router_gemm_kernel<256, 2, 3>), grid, dim3(512), 0, stream, x, parts, bias, dst, T, d, E,
+                           n_mblocks, n_nblocks, S);
     if (S > 1) {
         const int64_t n = T * E;
         const int64_t rb = std::min<int64_t>((n + 255) / 256, 8192);

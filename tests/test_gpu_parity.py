@@ -136,10 +136,14 @@ ROUTE_CASES = [
     ("many_expert", dict(T=130, d=384, E=130, k=16, h=128)),
     ("skewed", dict(T=67, d=128, E=96, k=16, h=128)),
     ("decode", dict(T=1, d=7168, E=384, k=8, h=128)),
+    # enough 256-token x 128-expert tiles for two rounds of the CUs: the 512-token tiles, without
+    # a K split (bias in the GEMM's epilogue), a partial last token block and expert block
+    ("skewed", dict(T=8411, d=256, E=1000, k=16, h=128)),
 ]
+ROUTE_IDS = ["tiny", "prefill", "many_expert", "skewed", "decode", "skewed_tall_tiles"]
 
 
-@pytest.mark.parametrize("base,over", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+@pytest.mark.parametrize("base,over", ROUTE_CASES, ids=ROUTE_IDS)
 def test_route_vs_oracle(dev, moe, base, over):
     cfg = scaled_config(base, **over) if over else CONFIGS[base]
     inp = make_inputs(cfg, experts=False)
