@@ -144,6 +144,24 @@ def test_latent_forward_matches_oracle(dev, moe, case):
     _check_stages(moe, dev, inp, fwd, out)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_latent_forward_random_shapes(dev, moe, seed):
+    """Seeded LatentMoE shapes: ragged token counts, latent widths below and above d, zero to three
+    shared experts."""
+    r = np.random.default_rng(3000 + seed)
+    E = int(r.integers(1, 65))
+    S = int(r.integers(0, 4))
+    over = dict(T=int(r.integers(1, 301)), d=int(r.choice([128, 256, 512])), l=int(r.choice([128, 256, 384])),
+                E=E, k=int(r.integers(1, min(E, 8) + 1)), h=int(r.choice([128, 256])), n_shared=S,
+                h_shared=int(r.choice([128, 256])) if S else 0)
+    cfg = scaled_latent("latent_tiny", name=f"latent_random_{seed}", seed=400 + seed, **over)
+    print(f"latent random {seed}: {cfg}", flush=True)
+    inp = make_latent_inputs(cfg)
+    inp_d = make_latent_inputs(cfg, device=dev, gen_device="cpu")
+    fwd, out = _run(moe, dev, inp_d)
+    _check_stages(moe, dev, inp, fwd, out)
+
+
 def test_latent_forward_deterministic(dev, moe):
     cfg = scaled_latent("latent_tiny", T=300, E=16, k=4)
     inp = make_latent_inputs(cfg, device=dev, gen_device="cpu")

@@ -194,6 +194,21 @@ CASES = {
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_mx_forward_matches_oracle(dev, moe, case):
     cfg = scaled_config("tiny", name=f"mx_{case}", seed=100 + len(case), **CASES[case])
+    _check_mx_layer(dev, moe, cfg, case)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mx_forward_random_shapes(dev, moe, seed):
+    """Seeded MX layer shapes: ragged token counts, K of one or two 512-blocks, up to 40 experts."""
+    r = np.random.default_rng(2000 + seed)
+    E = int(r.integers(1, 41))
+    over = dict(T=int(r.integers(1, 401)), d=int(r.choice([512, 1024])), E=E,
+                k=int(r.integers(1, min(E, 8) + 1)), h=int(r.choice([512, 1024])))
+    cfg = scaled_config("skewed" if seed % 2 else "prefill", name=f"mx_random_{seed}", seed=300 + seed, **over)
+    _check_mx_layer(dev, moe, cfg, f"random {seed} {over}")
+
+
+def _check_mx_layer(dev, moe, cfg, case):
     print(f"mx case {case}: {cfg}", flush=True)
     inp = make_inputs(cfg)
     di = inp.to(dev)

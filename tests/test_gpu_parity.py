@@ -321,6 +321,30 @@ LAYER_CASES = [
 ]
 
 
+def _random_layer_shape(seed):
+    """A seeded layer shape: ragged token counts, widths of 1 to 5 K blocks, any expert count up to 160,
+    every top-k up to 16, with and without the skewed workload's gate bias."""
+    r = np.random.default_rng(1000 + seed)
+    E = int(r.integers(1, 161))
+    k = int(r.integers(1, min(E, 16) + 1))
+    return ("skewed" if seed % 2 else "prefill"), dict(T=int(r.integers(1, 601)), d=int(r.choice([128, 256, 384, 640])),
+                                                       E=E, k=k, h=int(r.choice([128, 256, 384])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_forward_random_shapes(dev, moe, seed):
+    base, over = _random_layer_shape(seed)
+    cfg = scaled_config(base, seed=50 + seed, **over)
+    print(f"[random layer] seed {seed}: {base} {over}", flush=True)
+    inp = make_inputs(cfg)
+    fwd, out, ref = _forward_and_oracle(moe, dev, inp, cfg)
+    gu.check_logits(ref["logits"], orc.gate_logits(inp.x, inp.w_router, inp.router_bias))
+    gu.check_route(fwd.intermediate("logits"), fwd.intermediate("topk_idx"), fwd.intermediate("topk_w"), cfg.k)
+    gu.check_permutation(fwd.intermediate("expert_offsets"), fwd.intermediate("row_of"),
+                         fwd.intermediate("row_src"), ref["idx"], cfg.E)
+    gu.check_layer(out, ref["out"])
+
+
 @pytest.mark.parametrize("base,over", LAYER_CASES, ids=[c[0] for c in LAYER_CASES])
 def test_forward_vs_oracle(dev, moe, base, over):
     cfg = scaled_config(base, **over) if over else CONFIGS[base]
