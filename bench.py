@@ -706,8 +706,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): this layer "
-              "build has no multi-GPU path; see the sharding notes in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}): the layer "
+              "runs on a single GPU and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
