@@ -172,6 +172,18 @@ def test_workspace_checks(lib):
     assert L.moe_workspace_bytes(ctypes.byref(s), 7) == 0
 
 
+def test_route_workspace_follows_the_k_split(lib):
+    """The router's workspace is its three bf16 weight parts plus, when K is split, one float32
+    partial sum per K range: 4 ranges at prefill (64 token x expert tiles), 32 at decode (3 tiles),
+    none once the tiles fill the CUs (many_expert: 512-token tiles, one round)."""
+    for (T, d, E), S in [((8192, 7168, 256), 4), ((128, 7168, 384), 32), ((16384, 7168, 896), 1),
+                         ((6144, 1024, 1024), 1)]:
+        s = lib.shape(T, d, E, 4, 128)
+        parts = 3 * 2 * ((E + 15) // 16 * 16) * d
+        want = (parts + 255) // 256 * 256 + (4 * S * T * E if S > 1 else 0)
+        assert lib.workspace_bytes(s, lib.MOE_CALL_ROUTE) == (want + 255) // 256 * 256, (T, d, E)
+
+
 def test_forward_workspace_layout(lib):
     """Every intermediate fits inside the forward workspace, aligned, without overlap."""
     for cfg in [GOOD, dict(T=8192, d=7168, E=256, k=4, h=2048), dict(T=16384, d=7168, E=896, k=16, h=1024),
