@@ -12,14 +12,15 @@
 // wavefront). Y rows and out are touched once, so both go through non-temporal
 // loads and stores that do not displace other data from the caches. Small work
 // items (T * d / 256 of them) keep every CU busy to the end of the launch.
-// Measured on MI355X: 5.97 TB/s at T = 8192, k = 4 and 5.75 TB/s at T = 16384,
-// k = 16 (d = 7168), against 4.9 TB/s for one wavefront per whole row.
+// Measured on MI355X (d = 7168): 5.8-5.9 TB/s at T = 8192, k = 4 and 5.7-5.9 TB/s
+// at T = 16384, k = 16, where 8 slots at a time gave 5.5 TB/s; one wavefront per
+// whole row gave 4.9 TB/s.
 #include "device_common.h"
 #include "launch.h"
 
 namespace moe {
 
-constexpr int kSlots = 8;       // slots whose loads are issued together
+constexpr int kSlots = 16;      // slots whose loads are issued together
 constexpr int kBlockCols = 256; // float columns per work item (one float4 per lane)
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y, int d,
