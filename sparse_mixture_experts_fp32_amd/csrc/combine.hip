@@ -8,21 +8,23 @@
 // j = 0..k-1, which makes the result bitwise repeatable.
 //
 // Bandwidth: each lane owns one float4 of the block; the loads of up to kSlots
-// slots are issued before the first multiply-add (kSlots KiB in flight per
-// wavefront). Y rows and out are touched once, so both go through non-temporal
+// slots (8, or 16 for more than 8 slots) are issued before the first
+// multiply-add (kSlots KiB in flight per wavefront). Y rows and out are touched once, so both go through non-temporal
 // loads and stores that do not displace other data from the caches. Small work
 // items (T * d / 256 of them) keep every CU busy to the end of the launch.
-// Measured on MI355X (d = 7168): 5.8-5.9 TB/s at T = 8192, k = 4 and 5.7-5.9 TB/s
-// at T = 16384, k = 16, where 8 slots at a time gave 5.5 TB/s; one wavefront per
-// whole row gave 4.9 TB/s.
+// Measured on MI355X (d = 7168): 5.8-6.0 TB/s at T = 8192, k = 4 and 5.7-6.0 TB/s
+// at T = 16384, k = 16, where 8 slots at a time gave 5.5 TB/s (16 slots at k = 4:
+// 5% slower); one wavefront per whole row gave 4.9 TB/s.
 #include "device_common.h"
 #include "launch.h"
 
 namespace moe {
 
-constexpr int kSlots = 16;      // slots whose loads are issued together
 constexpr int kBlockCols = 256; // float columns per work item (one float4 per lane)
 
+// kSlots: slots whose loads are issued together (16 VGPR-heavy slots halve the occupancy, so they pay
+// only when a token has more than 8 slots to fetch)
+template <int kSlots>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Y, int d,
                                                       const int32_t* __restrict__ row_of,
                                                       const float* __restrict__ w, int64_t T, int k,
@@ -77,8 +79,11 @@ hipError_t launch_combine(const float* y_rows, const int32_t* row_of, const floa
     if (T <= 0) return hipSuccess;
     const int64_t items = T * ((d + kBlockCols - 1) / kBlockCols);
     if ((items + 3) / 4 > INT32_MAX) return hipErrorInvalidValue;  // beyond one launch's grid
-    hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>((items + 3) / 4)), dim3(256), 0, stream, y_rows,
-                       d, row_of, topk_w, T, k, n_rows, out);
+    const dim3 grid(static_cast<unsigned>((items + 3) / 4));
+    if (k > 8)
+        hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(256), 0, stream, y_rows, d, row_of, topk_w, T, k, n_rows, out);
+    else
+        hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(256), 0, stream, y_rows, d, row_of, topk_w, T, k, n_rows, out);
     return hipGetLastError();
 }
 
