@@ -60,13 +60,21 @@ __device__ __forceinline__ uint32_t e2m1_mag(float y) {
     return static_cast<uint32_t>(((e + 1) << 1) + static_cast<int>(m));
 }
 
-// Magnitude code of y in E4M3 (7 bits), round to nearest even, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_mag(float y) {
-    if (y >= 448.f) return 0x7eu;
-    if (y < 0.015625f) return static_cast<uint32_t>(rintf(y * 512.f));     // subnormals, 8 -> 2^-6
-    const int e = floor_log2(y);                                           // -6 .. 8
-    const float m = rintf((ldexpf(y, -e) - 1.f) * 8.f);                    // 0 .. 8 (8 carries)
-    return static_cast<uint32_t>(((e + 7) << 3) + static_cast<int>(m));
+// Codes of four elements v[0..3] in E4M3 scaled by 2^-s, packed into one word (element i in byte i):
+// y = |v| / 2^s (exact: a power-of-two scaling), capped at the largest value 448, rounded to the
+// nearest value with ties to the even code by the matrix cores' float32 -> E4M3 conversion (for every
+// float32 y in [0, 448] it equals the rounding the OCP MX conversion defines), and the sign of v on
+// top, also where y rounds to zero.
+__device__ __forceinline__ uint32_t e4m3_codes4(const float* v, int s) {
+    float y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = fminf(ldexpf(fabsf(v[i]), -s), 448.f);
+    int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    packed = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], packed, true);
+    uint32_t sign = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sign |= signbit(v[i]) ? (0x80u << (8 * i)) : 0u;
+    return static_cast<uint32_t>(packed) | sign;
 }
 
 template <class In>
@@ -123,12 +131,9 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const In* __restrict__
         *reinterpret_cast<uint4*>(q + wcode_offset(row, kb, K)) = make_uint4(w[0], w[1], w[2], w[3]);
         scales[wscale_offset(row, kb, K)] = static_cast<uint8_t>(s + 127);
     } else {
-        uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+        uint32_t w[8];
 #pragma unroll
-        for (int i = 0; i < kMxBlock; ++i) {
-            const uint32_t c = e4m3_mag(ldexpf(fabsf(v[i]), -s)) | (signbit(v[i]) ? 0x80u : 0u);
-            w[i / 4] |= c << (8 * (i % 4));
-        }
+        for (int i = 0; i < 8; ++i) w[i] = e4m3_codes4(v + 4 * i, s);
         uint4* dst = reinterpret_cast<uint4*>(q + row * K + kb * kMxBlock);
         dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
         dst[1] = make_uint4(w[4], w[5], w[6], w[7]);

@@ -111,6 +111,32 @@ def test_mx_quantize_rows_bitexact(dev, moe, dtype, R, K):
     assert np.array_equal(_u8(sc), s_ref)
 
 
+def test_mx_quantize_rows_every_e4m3_boundary(dev, moe):
+    """float32 blocks led by 500 (shared exponent 0, so every other element is its own scaled value):
+    every E4M3 value, every midpoint between neighbouring values (a tie) and the float32 numbers just
+    below and above it, the saturating range 448 .. 500, all with both signs; codes bit for bit."""
+    vals = np.array(sorted(mx.E4M3["table"].values()))
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)
+    pts = np.concatenate([vals.astype(np.float32), mids, np.nextafter(mids, np.float32(0)),
+                          np.nextafter(mids, np.float32(1e9)), np.linspace(448, 500, 209, dtype=np.float32)])
+    pts = np.concatenate([pts, -pts])
+    n_blocks = -(-len(pts) // 31)
+    n_blocks += -n_blocks % 16
+    body = np.zeros(n_blocks * 31, dtype=np.float32)
+    body[:len(pts)] = pts
+    blocks = np.zeros((n_blocks, 32), dtype=np.float32)
+    blocks[:, 0] = 500.0
+    blocks[:, 1:] = body.reshape(n_blocks, 31)
+    x = blocks.reshape(n_blocks // 16, 512)
+    q, sc = moe.moe_mx_quantize_rows(torch.from_numpy(x).to(dev))
+    torch.cuda.synchronize()
+    codes_ref, s_ref = mx.quantize(x.astype(np.float64), mx.E4M3)
+    assert np.all(s_ref == 127)
+    bad = np.argwhere(_u8(q) != codes_ref)
+    assert bad.size == 0, f"E4M3 codes differ at {bad[:5].tolist()}: inputs {x[tuple(bad[:5].T)].tolist()}"
+    assert np.array_equal(_u8(sc), s_ref)
+
+
 # ------------------------------------------------------------- the layer
 
 def _mx_weights(moe, inp, dev):
